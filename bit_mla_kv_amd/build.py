@@ -1,0 +1,57 @@
+"""Build the gfx950 HIP library libmla_lowbit.so in-tree with hipcc.
+
+Each translation unit is compiled separately (the writer with
+-ffp-contract=off so the quantizer's fp32 steps are never fused) and linked
+into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmla_lowbit.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+          # packed fp32 VALU forms are kept out of generated code
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(HERE, "..", "include")]
+UNITS = {
+    "append.hip": ["-ffp-contract=off"],
+    "decode.hip": [],
+    "abi.hip": [],
+}
+
+
+def _compile(unit: str, extra: list[str]) -> str:
+    obj = os.path.join(BUILD, unit + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, unit), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError(f"hipcc failed for {unit}")
+    return obj
+
+
+def build() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
+        objs = list(ex.map(lambda kv: _compile(*kv), UNITS.items()))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

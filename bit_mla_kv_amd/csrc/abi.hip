@@ -1,0 +1,196 @@
+// Host side of the C ABI declared in include/mla_lowbit.h: argument checks,
+// status strings, the thread-local error message and the kernel launches.
+// Nothing here allocates device memory or synchronises the stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mla_lowbit.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_layout(const mla_lowbit_layout* L) {
+  if (!L) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "layout is NULL");
+  if (L->abi_version != MLA_LOWBIT_ABI_VERSION)
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "abi_version %d, library implements %d", L->abi_version,
+                MLA_LOWBIT_ABI_VERSION);
+  if (L->d_c != mla::kDc || L->d_r != mla::kDr || L->group != mla::kGroup || L->page_tokens != mla::kPageTokens)
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "layout (d_c=%d, d_r=%d, group=%d, page_tokens=%d) unsupported; "
+                "need (512, 64, 64, 64)", L->d_c, L->d_r, L->group, L->page_tokens);
+  if ((L->bits_c != 4 && L->bits_c != 2) || L->bits_r != 4)
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "bits (c=%d, r=%d) unsupported; need c in {4,2}, r = 4", L->bits_c,
+                L->bits_r);
+  if (L->n_sink < 0 || L->n_sink > 64 || L->n_recent < 1 || L->n_recent > 8192)
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "n_sink=%d / n_recent=%d outside [0,64] / [1,8192]", L->n_sink,
+                L->n_recent);
+  return MLA_LOWBIT_OK;
+}
+
+int check_cache(const mla_lowbit_cache* c) {
+  if (!c) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "cache is NULL");
+  int st = check_layout(&c->layout);
+  if (st != MLA_LOWBIT_OK) return st;
+  if (c->num_pages < 0 || c->num_slots < 0 || c->max_pages_per_seq < 0)
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "negative cache dimension");
+  if (c->num_pages > 0 && (!c->pages || !aligned(c->pages, 256)))
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "pages must be a non-NULL 256-byte aligned device pointer");
+  if (c->num_slots > 0) {
+    if (!c->recent || !aligned(c->recent, 16))
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "recent must be a non-NULL 16-byte aligned device pointer");
+    if (c->layout.n_sink > 0 && (!c->sink || !aligned(c->sink, 16)))
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "sink must be a non-NULL 16-byte aligned device pointer");
+    if (c->max_pages_per_seq > 0 && !c->block_table)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "block_table is NULL");
+  }
+  return MLA_LOWBIT_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_LOWBIT_OK;
+  return fail(MLA_LOWBIT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t lse_off, o_off, total;
+};
+
+WsLayout ws_layout(int batch, int heads, int n_splits) {
+  WsLayout w;
+  const size_t rows = (size_t)batch * n_splits * heads;
+  w.lse_off = 0;
+  w.o_off = align_up(rows * sizeof(float), 256);
+  w.total = w.o_off + rows * mla::kDc * sizeof(float);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_lowbit_page_bytes(const mla_lowbit_layout* layout) {
+  if (check_layout(layout) != MLA_LOWBIT_OK) return 0;
+  return (size_t)mla::page_bytes(layout->bits_c);
+}
+
+int mla_lowbit_quantize_append(const mla_lowbit_cache* cache, const void* kv_new, const int32_t* token_slot,
+                               const int32_t* token_pos, const int32_t* slot_len_after, int32_t n_tokens,
+                               void* stream) {
+  int st = check_cache(cache);
+  if (st != MLA_LOWBIT_OK) return st;
+  if (n_tokens < 0) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "n_tokens = %d < 0", n_tokens);
+  if (n_tokens == 0) return MLA_LOWBIT_OK;
+  if (!kv_new || !aligned(kv_new, 16)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "kv_new must be 16-byte aligned");
+  if (!token_slot || !token_pos || !slot_len_after)
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "token_slot, token_pos and slot_len_after must be non-NULL");
+  if (cache->num_slots == 0) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "cache has no slots");
+  mla::AppendParams p;
+  p.pages = static_cast<uint8_t*>(cache->pages);
+  p.num_pages = cache->num_pages;
+  p.sink = static_cast<uint16_t*>(cache->sink);
+  p.recent = static_cast<uint16_t*>(cache->recent);
+  p.num_slots = cache->num_slots;
+  p.block_table = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.n_sink = cache->layout.n_sink;
+  p.n_recent = cache->layout.n_recent;
+  p.bits_c = cache->layout.bits_c;
+  p.kv = static_cast<const uint16_t*>(kv_new);
+  p.token_slot = token_slot;
+  p.token_pos = token_pos;
+  p.slot_len_after = slot_len_after;
+  p.n_tokens = n_tokens;
+  return device_status(mla::launch_append(p, static_cast<hipStream_t>(stream)), "quantize_append launch");
+}
+
+size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_t batch, int32_t num_heads,
+                                         int32_t max_seq_len) {
+  if (check_layout(layout) != MLA_LOWBIT_OK || batch < 0 || max_seq_len < 0) return 0;
+  mla::DecodeConfig cfg;
+  if (!mla::decode_config(num_heads, layout->n_sink, layout->n_recent, batch, max_seq_len, &cfg)) return 0;
+  return ws_layout(batch, num_heads, cfg.n_splits).total;
+}
+
+int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
+                      int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_cache(cache);
+  if (st != MLA_LOWBIT_OK) return st;
+  if (batch < 0 || max_seq_len < 0)
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "batch=%d max_seq_len=%d must be >= 0", batch, max_seq_len);
+  mla::DecodeConfig cfg;
+  if (!mla::decode_config(num_heads, cache->layout.n_sink, cache->layout.n_recent, batch, max_seq_len, &cfg))
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "num_heads=%d unsupported (16, 32, 64 or a multiple of 128)",
+                num_heads);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (batch == 0) return MLA_LOWBIT_OK;
+  if (!q || !aligned(q, 16)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "q must be a 16-byte aligned device pointer");
+  if (!out || !aligned(out, 16))
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
+  if (!seq_slot || !seq_len) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "seq_slot and seq_len must be non-NULL");
+  if (lse && !aligned(lse, 4)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const WsLayout wl = ws_layout(batch, num_heads, cfg.n_splits);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(MLA_LOWBIT_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
+  if (workspace_bytes < wl.total)
+    return fail(MLA_LOWBIT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  if (cache->num_slots == 0) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "cache has no slots");
+
+  mla::DecodeParams p;
+  p.pages = static_cast<const uint8_t*>(cache->pages);
+  p.num_pages = cache->num_pages;
+  p.sink = static_cast<const uint16_t*>(cache->sink);
+  p.recent = static_cast<const uint16_t*>(cache->recent);
+  p.num_slots = cache->num_slots;
+  p.block_table = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.n_sink = cache->layout.n_sink;
+  p.n_recent = cache->layout.n_recent;
+  p.q = static_cast<const uint16_t*>(q);
+  p.seq_slot = seq_slot;
+  p.seq_len = seq_len;
+  p.batch = batch;
+  p.heads = num_heads;
+  p.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
+  p.pages_per_split = cfg.pages_per_split;
+  p.n_splits = cfg.n_splits;
+  p.head_groups = num_heads / cfg.heads_per_wg;
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse_off);
+  p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = device_status(mla::launch_decode(p, cache->layout.bits_c, s), "decode launch");
+  if (st != MLA_LOWBIT_OK) return st;
+  return device_status(mla::launch_combine(p, s), "combine launch");
+}
+
+const char* mla_lowbit_status_string(int status) {
+  switch (status) {
+    case MLA_LOWBIT_OK: return "ok";
+    case MLA_LOWBIT_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_LOWBIT_ERR_UNSUPPORTED: return "unsupported layout or shape";
+    case MLA_LOWBIT_ERR_WORKSPACE: return "workspace too small";
+    case MLA_LOWBIT_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_lowbit_last_error(void) { return g_err; }
+
+}  // extern "C"

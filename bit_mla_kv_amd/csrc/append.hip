@@ -1,0 +1,130 @@
+// Fused quantize-append writer for the low-bit MLA cache (gfx950).
+//
+// One wavefront per new token, one lane per channel of each 64-channel group.
+// Per group: wave-wide min/max, scale s = bf16(fp32(max - min) / (2^b - 1)),
+// zero z = min, codes rint_half_even(fp32(x - min) / s) clamped to [0, 2^b-1]
+// (per-token asymmetric affine quantizer, group size 64: ai.info summary,
+// "Methodology in Plain English"; onedev.kr review, "Premises and limits").
+// Codes are OR-reduced across lanes into packed dwords and stored with the
+// group's metadata dword into the token's page row; the bf16 row is copied to
+// the sink buffer (first n_sink positions) and to the recent ring (last
+// n_recent positions of the slot after this call), which is the whole of the
+// migration rule: a token that leaves the window is served from the packed
+// copy written here (onedev.kr review, "How it is used").
+//
+// Built with -ffp-contract=off; the arithmetic has no a*b+c anyway.
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t or_reduce(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= p.n_tokens) return;
+  const int slot = p.token_slot[tok];
+  const int pos = p.token_pos[tok];
+  if (slot < 0 || slot >= p.num_slots || pos < 0) return;
+  const uint16_t* row = p.kv + (int64_t)tok * kD;
+
+  // page row of this token (skip packed write if the table entry is out of range)
+  uint8_t* prow_c = nullptr;
+  uint8_t* prow_r = nullptr;
+  uint32_t* prow_m = nullptr;
+  const int pidx = pos / kPageTokens;
+  if (pidx < p.max_pages) {
+    const int64_t page = p.block_table[(int64_t)slot * p.max_pages + pidx];
+    if (page >= 0 && page < p.num_pages) {
+      const int r = pos % kPageTokens;
+      const int cb = content_row_bytes(p.bits_c);
+      uint8_t* base = p.pages + page * (int64_t)page_bytes(p.bits_c);
+      prow_c = base + r * cb;
+      prow_r = base + kPageTokens * cb + r * (kDr / 2);
+      prow_m = reinterpret_cast<uint32_t*>(base + kPageTokens * (cb + kDr / 2)) + r * kGroups;
+    }
+  }
+
+  if (prow_c) {
+#pragma unroll 1
+    for (int g = 0; g < kGroups; ++g) {
+      const int bits = g < 8 ? p.bits_c : 4;
+      const int lb = (1 << bits) - 1;
+      const float x = bf16_to_float(row[g * kGroup + lane]);
+      const float mn = wave_min(x);
+      const float mx = wave_max(x);
+      const float range = mx - mn;
+      const float s32 = __fdiv_rn(range, (float)lb);
+      uint16_t sb = float_to_bf16_rne(s32);
+      if ((sb & 0x7FFFu) == 0) sb = 0;  // a zero scale is stored as +0
+      const float s = bf16_to_float(sb);
+      uint16_t zb = float_to_bf16_rne(mn);  // exact: mn is a bf16 value
+      if (zb == 0x8000u) zb = 0;             // -0 stored as +0
+      uint32_t code = 0;
+      if (s != 0.0f) {
+        float d = __builtin_rintf(__fdiv_rn(x - mn, s));
+        d = fminf(fmaxf(d, 0.0f), (float)lb);
+        code = (uint32_t)d;
+      }
+      if (bits == 4) {
+        const uint32_t w = or_reduce<8>(code << (4 * (lane & 7)));
+        if ((lane & 7) == 0) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(g < 8 ? prow_c : prow_r);
+          dst[((g < 8 ? g : 0) * kGroup + lane) / 8] = w;
+        }
+      } else {  // 2-bit content
+        const uint32_t w = or_reduce<16>(code << (2 * (lane & 15)));
+        if ((lane & 15) == 0) reinterpret_cast<uint32_t*>(prow_c)[(g * kGroup + lane) / 16] = w;
+      }
+      if (lane == 0) prow_m[g] = (uint32_t)sb | ((uint32_t)zb << 16);
+    }
+  }
+
+  // bf16 copies: 1152 bytes = 72 x 16 bytes per row
+  const uint4* src = reinterpret_cast<const uint4*>(row);
+  if (pos < p.n_sink) {
+    uint4* dst = reinterpret_cast<uint4*>(p.sink + ((int64_t)slot * p.n_sink + pos) * kD);
+    for (int i = lane; i < kD / 8; i += 64) dst[i] = src[i];
+  }
+  if (pos >= p.slot_len_after[slot] - p.n_recent) {
+    uint4* dst = reinterpret_cast<uint4*>(p.recent + ((int64_t)slot * p.n_recent + pos % p.n_recent) * kD);
+    for (int i = lane; i < kD / 8; i += 64) dst[i] = src[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  if (p.n_tokens <= 0) return hipSuccess;
+  const int blocks = (p.n_tokens + 3) / 4;
+  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,180 @@
+/*
+ * mla_lowbit.h - C ABI of the MI355X (gfx950) low-bit MLA KV-cache library.
+ *
+ * The library implements the decode hot path of QuantMLA's low-bit
+ * Multi-Head Latent Attention cache (QuantMLA: Function-Aligned Dual-Path
+ * Quantization for Low-Bit MLA KV Caching):
+ *
+ *  - every token's content latent c (d_c = 512) and decoupled RoPE key k_r
+ *    (d_r = 64) are quantized per token, asymmetrically, in groups of 64
+ *    channels, with one bf16 scale and one bf16 zero per group (ai.info
+ *    summary, "Methodology in Plain English", last paragraph; onedev.kr
+ *    review, "Premises and limits");
+ *  - content codes are 4 or 2 bits, RoPE-key codes 4 bits (C4R4 / C2R4;
+ *    ai.info summary, "Key Contributions", item 3);
+ *  - a fused writer keeps a packed copy of every token plus the original
+ *    bf16 rows of the first 4 ("sink") and the most recent 128 tokens
+ *    (onedev.kr review, "How it is used"; ai.info summary, "Key
+ *    Contributions", item 4);
+ *  - decode attends over all valid tokens with one global softmax, each
+ *    token entering exactly once: from its bf16 row when it is a sink or
+ *    recent token, otherwise from its packed copy, unpacked and dequantized
+ *    inside the attention loop (same sources).
+ *
+ * Conventions for every entry point
+ *  - All buffer pointers are DEVICE pointers (HIP device memory), except the
+ *    mla_lowbit_layout / mla_lowbit_cache structs themselves, which are read
+ *    on the host during the call.  "bf16" buffers hold IEEE bfloat16 bit
+ *    patterns (uint16).
+ *  - The caller allocates and owns every buffer (cache, queries, outputs,
+ *    workspace).  The library allocates no device memory and keeps no
+ *    pointer after a call returns.
+ *  - Calls are asynchronous and ordered on the given stream (hipStream_t
+ *    passed as void*; NULL is the null stream).  An append must be issued
+ *    before the decode that reads it, on the same stream (or with a
+ *    dependency the caller creates).
+ *  - Every entry point returns MLA_LOWBIT_OK or an error status.  Host-side
+ *    argument checks run before anything is enqueued; on error nothing is
+ *    enqueued and mla_lowbit_last_error() holds a message (thread-local).
+ *    Launch failures return MLA_LOWBIT_ERR_DEVICE with the HIP message.
+ *  - Device-resident index data (block_table entries, token positions,
+ *    slots, sequence lengths) is the caller's contract: kernels skip writes
+ *    and reads whose indices fall outside the buffers described by the
+ *    structs, but results for such inputs are unspecified.
+ *  - Values are staged through fp16 inside decode: cache rows and queries
+ *    must have |x| < 65504 (finite); NaN/Inf inputs are out of contract.
+ *
+ * Supported layout: d_c = 512, d_r = 64, group = 64, page_tokens = 64,
+ * bits_c in {4, 2}, bits_r = 4, 0 <= n_sink <= 64, 1 <= n_recent <= 8192
+ * (n_recent >= every sequence length gives an all-bf16 cache).  num_heads
+ * must be 16, 32, 64 or a multiple of 128.  Anything else returns
+ * MLA_LOWBIT_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_LOWBIT_H_
+#define MLA_LOWBIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_LOWBIT_ABI_VERSION 1
+
+enum {
+  MLA_LOWBIT_OK = 0,
+  MLA_LOWBIT_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad count */
+  MLA_LOWBIT_ERR_UNSUPPORTED = 2, /* layout or head count this build does not implement */
+  MLA_LOWBIT_ERR_WORKSPACE = 3,   /* workspace smaller than mla_lowbit_decode_workspace_bytes() */
+  MLA_LOWBIT_ERR_DEVICE = 4       /* HIP launch / runtime error */
+};
+
+/* Shape and precision of the cache (mixed-precision policy included). */
+typedef struct mla_lowbit_layout {
+  int32_t abi_version; /* = MLA_LOWBIT_ABI_VERSION */
+  int32_t d_c;         /* content latent width: 512 */
+  int32_t d_r;         /* RoPE key width: 64 */
+  int32_t bits_c;      /* content code bits: 4 (C4R4) or 2 (C2R4) */
+  int32_t bits_r;      /* RoPE-key code bits: 4 */
+  int32_t group;       /* channels per quantization group: 64 */
+  int32_t page_tokens; /* tokens per cache page: 64 */
+  int32_t n_sink;      /* leading tokens served from bf16: 4 */
+  int32_t n_recent;    /* most recent tokens served from bf16: 128 */
+} mla_lowbit_layout;
+
+/*
+ * The paged cache.  One page holds page_tokens consecutive tokens of one
+ * sequence slot as three contiguous arrays (structure of arrays):
+ *   [content codes: page_tokens x (d_c*bits_c/8) bytes]
+ *   [RoPE-key codes: page_tokens x (d_r*bits_r/8) bytes]
+ *   [metadata: page_tokens x 9 uint32]      (groups 0..7 content, 8 RoPE key)
+ * Codes are packed low bits first in channel order (4-bit: byte k holds
+ * channels 2k | 2k+1 << 4; 2-bit: byte k holds channels 4k .. 4k+3 at bit
+ * offsets 0, 2, 4, 6).  A metadata dword holds bf16 scale s in bits 0..15 and
+ * bf16 zero z in bits 16..31; a code q dequantizes to s*q + z.
+ * Token t of slot i lives in page block_table[i*max_pages_per_seq + t/64],
+ * row t%64.  Pages must be 256-byte aligned (the pool base must be).
+ */
+typedef struct mla_lowbit_cache {
+  mla_lowbit_layout layout;
+  void* pages;                /* [num_pages][page_bytes] */
+  int64_t num_pages;
+  void* sink;                 /* bf16 [num_slots][n_sink][d_c+d_r]; row i = token i */
+  void* recent;               /* bf16 [num_slots][n_recent][d_c+d_r]; row p % n_recent = token p */
+  int32_t num_slots;
+  const int32_t* block_table; /* [num_slots][max_pages_per_seq] physical page ids */
+  int32_t max_pages_per_seq;
+} mla_lowbit_cache;
+
+/* Bytes per cache page for this layout; 0 if the layout is unsupported. */
+size_t mla_lowbit_page_bytes(const mla_lowbit_layout* layout);
+
+/*
+ * Fused quantize-append writer (onedev.kr review, "How it is used": the
+ * writer keeps packed copies of all tokens and the bf16 values of the sink
+ * and recent tokens).
+ *
+ * kv_new         bf16 [n_tokens][d_c+d_r], rows c || k_r (k_r after RoPE);
+ *                16-byte aligned.
+ * token_slot     int32 [n_tokens]: cache slot of each new token.
+ * token_pos      int32 [n_tokens]: absolute position of the token in its
+ *                sequence (0-based).
+ * slot_len_after int32 [num_slots]: length of each slot once this call's
+ *                tokens are in (only entries of slots named in token_slot
+ *                are read).
+ *
+ * For every token: quantizes its 9 groups (per-token asymmetric affine,
+ * group 64; scale s = bf16(fp32(max-min)/(2^b-1)), zero z = min, codes
+ * rint_half_even((x-min)/s) clamped), packs codes and metadata into its page
+ * row, copies the bf16 row into sink row pos when pos < n_sink, and into
+ * recent row pos % n_recent when pos >= slot_len_after[slot] - n_recent.
+ * A token that leaves the recent window is served from the packed copy
+ * written here; nothing is re-quantized.  Tokens of one call must have
+ * distinct (slot, pos).  n_tokens = 0 is a no-op.
+ */
+int mla_lowbit_quantize_append(const mla_lowbit_cache* cache, const void* kv_new, const int32_t* token_slot,
+                               const int32_t* token_pos, const int32_t* slot_len_after, int32_t n_tokens,
+                               void* stream);
+
+/* Workspace bytes mla_lowbit_decode needs for this batch shape (0 on
+ * unsupported arguments). */
+size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_t batch, int32_t num_heads,
+                                         int32_t max_seq_len);
+
+/*
+ * Low-bit absorbed-MLA decode, one query token per sequence (ai.info
+ * summary, "Key Contributions", item 4; onedev.kr review, "How it is used").
+ *
+ * q           bf16 [batch][num_heads][d_c+d_r] = absorbed q_c || q_r; 16-byte aligned.
+ * seq_slot    int32 [batch]: cache slot of each sequence.
+ * seq_len     int32 [batch]: valid tokens N of each sequence (0 <= N <= max_seq_len),
+ *             counting the token appended for this step.
+ * softmax_scale  fp32 scale applied to q_c.c + q_r.k_r.
+ * out         bf16 [batch][num_heads][d_c]: softmax(scores) . c over the N
+ *             tokens; N = 0 gives zeros.  16-byte aligned.
+ * lse         fp32 [batch][num_heads] natural-log log-sum-exp of the scaled
+ *             scores (-inf for N = 0); may be NULL.
+ * workspace   device scratch of at least mla_lowbit_decode_workspace_bytes(),
+ *             256-byte aligned; contents need no initialisation.
+ *
+ * Token t of a sequence is read from its bf16 row when t < n_sink or
+ * t >= N - n_recent, otherwise from its packed copy.  The work is split
+ * along the context into page-aligned chunks whose partial results are
+ * merged exactly with a log-sum-exp combine.
+ */
+int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
+                      int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* mla_lowbit_status_string(int status);
+
+/* Thread-local detail message of the last non-OK return on this thread. */
+const char* mla_lowbit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LOWBIT_H_ */

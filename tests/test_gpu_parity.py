@@ -1,0 +1,279 @@
+"""GPU parity of the HIP path against the CPU oracle (marked gpu).
+
+Writer: packed pages, sink and ring bytes are bit-exact with the oracle's
+quantize + placement.  Decode: outputs within E <= 2e-3 (tests/parity.py),
+lse within 1e-3, plus invariances (page order, split count, run-to-run,
+stream vs bulk append) and NaN canaries proving each token is read exactly
+once from exactly one representation.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import oracle
+from parity import E_TOL, LSE_TOL, bf16_tensor_to_f64, e_metric, reference
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_mla_kv_amd as m
+from bit_mla_kv_amd import cache_builder as cb
+
+SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
+
+
+def build(rows_per_seq, bits_c, seed=0, n_sink=4, n_recent=128, spare_tokens=0, perm_seed=None):
+    lens = [r.shape[0] for r in rows_per_seq]
+    layout = m.make_layout(bits_c, n_sink, n_recent)
+    need = [max(1, (n + spare_tokens + 63) // 64) for n in lens]
+    total = sum(need) + 3
+    perm = mi.page_permutation(seed if perm_seed is None else perm_seed, total)
+    cache = cb.allocate_for(layout, lens, perm, spare_tokens=spare_tokens)
+    for b, rows in enumerate(rows_per_seq):
+        if rows.shape[0]:
+            cb.prefill(cache, b, rows)
+    torch.cuda.synchronize()
+    return cache
+
+
+def run_decode(cache, q_u16, lens, max_len=None):
+    B, H = q_u16.shape[0], q_u16.shape[1]
+    dev = cache.pages.device
+    max_len = max(lens) if max_len is None else max_len
+    q = cb.to_device_bf16(q_u16.reshape(B * H, -1), dev).view(B, H, 576)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(cache.layout, B, H, max(max_len, 1), dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    m.decode(cache, q, slots, sl, max(max_len, 1), SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(out, lse, ref_o, ref_l, tag=""):
+    o = bf16_tensor_to_f64(out)
+    E = e_metric(o, ref_o)
+    assert np.all(np.isfinite(o)), tag
+    assert E.max() <= E_TOL, f"{tag} E max {E.max():.3e} at {np.unravel_index(E.argmax(), E.shape)}"
+    l = lse.cpu().numpy().astype(np.float64)
+    both_inf = np.isneginf(l) & np.isneginf(ref_l)
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(l - ref_l))
+    assert err.max() <= LSE_TOL, f"{tag} lse err {err.max():.3e}"
+    return E.max()
+
+
+# ------------------------------------------------------------------- writer
+def expected_pool(cache, rows_per_seq, bits_c):
+    pool = np.zeros(tuple(cache.pages.shape), np.uint8)
+    bt = cache.block_table.cpu().numpy()
+    for b, rows in enumerate(rows_per_seq):
+        if rows.shape[0]:
+            cc, cr, meta = oracle.quantize(rows, bits_c)
+            oracle.place_pages(pool, bt[b], cc, cr, meta, bits_c)
+    return pool
+
+
+def check_bf16_buffers(cache, rows_per_seq, n_sink=4, n_recent=128):
+    sink = cache.sink.view(torch.int16).cpu().numpy().view(np.uint16)
+    ring = cache.recent.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, rows in enumerate(rows_per_seq):
+        s, r = oracle.bf16_buffers(rows, n_sink, n_recent)
+        for i, v in s.items():
+            assert np.array_equal(sink[b, i], v), (b, i)
+        for i, v in r.items():
+            assert np.array_equal(ring[b, i], v), (b, i)
+
+
+@pytest.mark.parametrize("bits_c", [4, 2])
+def test_writer_bitexact(bits_c):
+    lens = [1024, 200, 131, 5, 0, 64]
+    rows = [mi.rows(21, b, n) for b, n in enumerate(lens)]
+    cache = build(rows, bits_c, seed=21)
+    pool = cache.pages.cpu().numpy()
+    exp = expected_pool(cache, rows, bits_c)
+    bad = np.argwhere(pool != exp)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first {bad[:4].tolist()}"
+    check_bf16_buffers(cache, rows)
+
+
+def test_writer_outlier_and_edge_values():
+    """Rows with huge dynamic range, constant groups and signed zeros stay bit-exact."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((256, 576)) * np.exp(rng.uniform(-30, 30, (256, 1)))
+    x[:, rng.choice(576, 16, replace=False)] *= 1000
+    rows = mi.to_bf16(x)
+    rows[3, 64:128] = rows[3, 64]
+    rows[4, :] = 0
+    rows[5, ::2] = 0x8000
+    for bits_c in (4, 2):
+        cache = build([rows], bits_c, seed=22)
+        assert np.array_equal(cache.pages.cpu().numpy(), expected_pool(cache, [rows], bits_c))
+
+
+def test_writer_stream_equals_bulk():
+    """Appending one token (or small chunks) at a time gives the same cache as one bulk append."""
+    n = 333
+    rows = mi.rows(23, 0, n)
+    bulk = build([rows], 4, seed=23)
+    layout = m.make_layout(4)
+    stream = cb.allocate_for(layout, [n], mi.page_permutation(23, 6 + 3))
+    cuts = [0, 1, 2, 3, 4, 5, 70, 71, 200, 201, 333]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        cb.prefill(stream, 0, rows[a:b], start=a, len_after=b)
+    torch.cuda.synchronize()
+    assert np.array_equal(stream.pages.cpu().numpy(), bulk.pages.cpu().numpy())
+    check_bf16_buffers(stream, [rows])
+
+
+# ------------------------------------------------------------------- decode
+def test_decode_tiny_c4r4():
+    """The tiny workload: batch 1, 16 heads, 1024 tokens."""
+    w = mi.workload("tiny_c4r4")
+    rows = [mi.rows(w.seed, 0, 1024)]
+    q = mi.queries(w.seed, 1, 16)
+    cache = build(rows, 4, seed=w.seed)
+    out, lse = run_decode(cache, q, [1024])
+    ro, rl = reference(rows, q, 4, SCALE)
+    check(out, lse, ro, rl, "tiny")
+
+
+EDGE_LENS = [0, 1, 3, 4, 5, 63, 64, 65, 131, 132, 133, 134, 196, 197, 198, 260, 700, 2049]
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("bits_c", [4, 2])
+def test_decode_edge_lengths(heads, bits_c):
+    seed = 30 + heads + bits_c
+    rows = [mi.rows(seed, b, n) for b, n in enumerate(EDGE_LENS)]
+    q = mi.queries(seed, len(EDGE_LENS), heads)
+    cache = build(rows, bits_c, seed=seed)
+    out, lse = run_decode(cache, q, EDGE_LENS)
+    ro, rl = reference(rows, q, bits_c, SCALE)
+    check(out, lse, ro, rl, f"H{heads} C{bits_c}")
+    o = bf16_tensor_to_f64(out)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0].cpu().numpy()))  # N = 0
+
+
+def test_decode_heads_256():
+    lens = [900, 3000]
+    rows = [mi.rows(41, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(41, 2, 256)
+    cache = build(rows, 4, seed=41)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = reference(rows, q, 4, SCALE)
+    check(out, lse, ro, rl, "H256")
+
+
+def test_all_bf16_mode():
+    """n_recent >= N: every token from bf16, equals standard attention (oracle in all-bf16 mode)."""
+    lens = [300, 1000]
+    rows = [mi.rows(42, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(42, 2, 16)
+    cache = build(rows, 4, seed=42, n_recent=1024)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = reference(rows, q, 4, SCALE, n_recent=1024)
+    check(out, lse, ro, rl, "all-bf16")
+
+
+def test_exactly_once_canaries():
+    """NaN in every representation a token must NOT be read from leaves the output unchanged."""
+    lens = [1000, 150, 2, 0]
+    rows = [mi.rows(43, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(43, len(lens), 16)
+    cache = build(rows, 4, seed=43)
+    out0, lse0 = run_decode(cache, q, lens)
+    bt = cache.block_table.cpu().numpy()
+    pages = cache.pages.cpu().numpy()
+    cbytes, meta_off = 256, 64 * (256 + 32)
+    nan_meta = np.frombuffer(np.array([0x7FC07FC0] * 9, np.uint32).tobytes(), np.uint8)
+    for b, n in enumerate(lens):
+        npg = max(1, (n + 63) // 64)
+        for t in range(npg * 64):
+            bf = t < 4 or t >= n - 128 or t >= n
+            if not bf:
+                continue
+            pg, r = bt[b, t // 64], t % 64
+            pages[pg, meta_off + 36 * r: meta_off + 36 * r + 36] = nan_meta
+            pages[pg, r * cbytes:(r + 1) * cbytes] = 0xFF
+    cache.pages.copy_(torch.from_numpy(pages))
+    ring = cache.recent.view(torch.int16).cpu().numpy()
+    sink = cache.sink.view(torch.int16).cpu().numpy()
+    for b, n in enumerate(lens):
+        live = {p % 128 for p in range(max(0, n - 128), n)}
+        for i in range(128):
+            if i not in live:
+                ring[b, i] = np.int16(0x7FC0)
+        for i in range(min(4, n), 4):
+            sink[b, i] = np.int16(0x7FC0)
+    cache.recent.copy_(torch.from_numpy(ring).view(torch.bfloat16))
+    cache.sink.copy_(torch.from_numpy(sink).view(torch.bfloat16))
+    out1, lse1 = run_decode(cache, q, lens)
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)
+    ro, rl = reference(rows, q, 4, SCALE)
+    check(out1, lse1, ro, rl, "canary")
+
+
+def test_page_order_invariance_and_determinism():
+    lens = [5000, 777]
+    rows = [mi.rows(44, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(44, 2, 64)
+    c1 = build(rows, 4, seed=44, perm_seed=1)
+    c2 = build(rows, 4, seed=44, perm_seed=2)
+    assert not torch.equal(c1.block_table, c2.block_table)
+    o1, l1 = run_decode(c1, q, lens)
+    o1b, l1b = run_decode(c1, q, lens)
+    o2, l2 = run_decode(c2, q, lens)
+    assert torch.equal(o1.view(torch.int16), o1b.view(torch.int16)) and torch.equal(l1, l1b)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_split_count_invariance():
+    lens = [9000, 4100]
+    rows = [mi.rows(45, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(45, 2, 16)
+    cache = build(rows, 4, seed=45)
+    ro, rl = reference(rows, q, 4, SCALE)
+    outs = []
+    for pps in ("1", "4", "37", "1000"):
+        os.environ["MLA_LOWBIT_PAGES_PER_SPLIT"] = pps
+        try:
+            out, lse = run_decode(cache, q, lens)
+        finally:
+            del os.environ["MLA_LOWBIT_PAGES_PER_SPLIT"]
+        check(out, lse, ro, rl, f"pps={pps}")
+        outs.append(bf16_tensor_to_f64(out))
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 4e-3 * np.max(np.abs(outs[0]))
+
+
+def test_serving_step_append_then_decode():
+    """One token appended per sequence (its predecessor 128 back migrates to packed), then decode."""
+    lens = [1500, 129, 4000, 10]
+    rows_full = [mi.rows(46, b, n + 3) for b, n in enumerate(lens)]
+    q = mi.queries(46, len(lens), 128)
+    layout = m.make_layout(4)
+    perm = mi.page_permutation(46, 200)
+    cache = cb.allocate_for(layout, lens, perm, spare_tokens=3)
+    for b, n in enumerate(lens):
+        cb.prefill(cache, b, rows_full[b][:n])
+    cur = list(lens)
+    for step in range(3):
+        kv = np.stack([rows_full[b][cur[b]] for b in range(len(lens))])
+        dev = cache.pages.device
+        slots = torch.arange(len(lens), dtype=torch.int32, device=dev)
+        pos = torch.tensor(cur, dtype=torch.int32, device=dev)
+        after = pos + 1
+        m.quantize_append(cache, cb.to_device_bf16(kv, dev), slots, pos, after)
+        cur = [c + 1 for c in cur]
+        out, lse = run_decode(cache, q, cur, max_len=max(lens) + 3)
+        ro, rl = reference([rows_full[b][:cur[b]] for b in range(len(lens))], q, 4, SCALE)
+        check(out, lse, ro, rl, f"step{step}")
