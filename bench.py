@@ -1,0 +1,285 @@
+"""Benchmark of the low-bit MLA decode hot path on one MI355X.
+
+One step = the whole path on one batch: the fused quantize-append of one new
+token per sequence (the writer, including the recent-window migration) and
+one split-KV decode + log-sum-exp combine over every sequence's full
+context.  Inputs are synthetic (seeded generator, shapes and value
+distributions of the pages' MLA models) and resident in HBM before timing.
+
+Prints one JSON line: KV tokens/s (sum of context lengths decoded per
+second), the decode kernel's roofline fraction (algorithmic bytes or flops
+per launch / its own duration from HIP events on its stream) and the CPU
+oracle's throughput on a bounded sample.
+
+    python bench.py [--workload dsv3_c4r4_128k] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "dsv3_c4r4_128k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--instances", type=int, default=3,
+                    help="cache copies rotated across steps so the 256 MB Infinity Cache cannot serve them")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def kv_bytes_per_token(bits_c: int) -> int:
+    return 512 * bits_c // 8 + 32 + 36
+
+
+def algorithmic(seq_lens, heads, bits_c, n_bf=132):
+    """Algorithmic bytes and flops of one decode over these lengths.
+
+    bytes/seq = packed bytes of non-bf16 tokens + 1152 B per bf16 token + 4 B per page-table entry
+                + H * (576*2 q + 512*2 out + 4 lse);  flops/seq = 2 * H * (576 + 512) * N."""
+    n = np.asarray(seq_lens, dtype=np.int64)
+    nb = np.minimum(n, n_bf)
+    by = kv_bytes_per_token(bits_c) * (n - nb) + 1152 * nb + 4 * ((n + 63) // 64) + heads * (1152 + 1024 + 4)
+    fl = 2 * heads * (576 + 512) * n
+    return int(by.sum()), int(fl.sum())
+
+
+class Hip:
+    """hipEvent timing through the HIP runtime (events recorded on the kernels' own stream)."""
+
+    def __init__(self):
+        import glob
+        cands = ["libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"] + glob.glob("/opt/rocm*/lib/libamdhip64.so*")
+        for c in cands:
+            try:
+                self.L = ctypes.CDLL(c)
+                break
+            except OSError:
+                continue
+        P = ctypes.c_void_p
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        self.L.hipEventRecord.argtypes = [P, P]
+        self.L.hipEventSynchronize.argtypes = [P]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        self.L.hipEventDestroy.argtypes = [P]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, ev, stream):
+        assert self.L.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.L.hipEventSynchronize(b) == 0
+        assert self.L.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands (quantize -> select -> exact fp64 attention), all heads, on the first
+    sequences of the workload, scaled to KV tokens/s."""
+    import mla_inputs as mi
+    import oracle
+    q = mi.queries(w.seed, w.batch, w.heads)
+    tokens, t_used, seqs, heads_done = 0, 0.0, 0, w.heads
+    order = np.argsort(-w.seq_lens)  # longest first
+    for b in order:
+        n = int(w.seq_lens[b])
+        rows = mi.rows(w.seed, int(b), n, threads=16)
+        t0 = time.perf_counter()
+        oracle.decode_sequence(rows, q[b], w.scale, w.bits_c)
+        t_used += time.perf_counter() - t0
+        tokens += n
+        seqs += 1
+        if t_used >= budget_s:
+            break
+    return {"value": tokens / t_used, "unit": "KV tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{seqs} sequence(s) x {heads_done} heads, {tokens} context tokens, quantize+select+"
+                      f"fp64 attention, {t_used:.1f} s wall"}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "mla_internal.h"):
+        h.update(open(os.path.join(ROOT, "bit_mla_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken on the
+    current decode source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"decode source digest: `([0-9a-f]+)`", txt)
+    m_val = re.search(r"HBM bytes per decode launch \(calibrated\): ([0-9.eE+]+)", txt)
+    if not (m_src and m_val) or m_src.group(1) != source_digest():
+        return None
+    return float(m_val.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the low-bit MLA decode path is built and timed on a single "
+              "MI355X (run without --gpus or with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_inputs as mi
+    import bit_mla_kv_amd as m
+    from bit_mla_kv_amd import cache_builder as cb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = mi.workload(args.workload)
+    B, H, bits = w.batch, w.heads, w.bits_c
+    total_steps = args.warmup + args.steps
+    R = max(1, args.instances)
+    # every instance receives one new token per sequence each R steps
+    grow = (total_steps + R - 1) // R
+    final_lens = w.seq_lens.astype(np.int64)
+    start_lens = np.maximum(final_lens - grow, 1) if w.steps_append == 0 else final_lens
+    max_len = int((start_lens + grow).max())
+    layout = m.make_layout(bits)
+
+    t_setup = time.perf_counter()
+    perm = mi.page_permutation(w.seed, int(((start_lens + grow + 63) // 64).sum()) + 8)
+    base = cb.allocate_for(layout, start_lens, perm, spare_tokens=grow, device=dev)
+    outl = mi.outlier_channels(w.seed)
+    new_rows = np.empty((grow, B, 576), np.uint16)
+    for b in range(B):
+        n0 = int(start_lens[b])
+        rows = mi.rows(w.seed, b, n0 + grow, outl, threads=16)
+        cb.prefill(base, b, rows[:n0])
+        new_rows[:, b] = rows[n0:n0 + grow]
+        del rows
+    torch.cuda.synchronize()
+    caches = [base]
+    for _ in range(R - 1):
+        c = m.PagedCache(layout, base.pages.clone(), base.sink.clone(), base.recent.clone(), base.block_table.clone())
+        caches.append(c)
+    lens = [start_lens.astype(np.int64).copy() for _ in range(R)]
+    q = cb.to_device_bf16(mi.queries(w.seed, B, H).reshape(B * H, -1), dev).view(B, H, 576)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(layout, B, H, max_len, dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    new_dev = cb.to_device_bf16(new_rows.reshape(grow * B, 576), dev).view(grow, B, 576)
+    # per-step positions / lengths, prepared before timing: step i appends at lens_i and decodes lens_i + 1
+    plan = []
+    for i in range(total_steps):
+        r = i % R
+        pos = lens[r].copy()
+        lens[r] += 1
+        plan.append((r, i // R, torch.tensor(pos, dtype=torch.int32, device=dev),
+                     torch.tensor(pos + 1, dtype=torch.int32, device=dev), pos + 1))
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hip = Hip()
+    ev_k = [(hip.event(), hip.event()) for _ in range(args.steps)]
+
+    def step(i, timed_idx=None):
+        r, k, pos, after, _ = plan[i]
+        m.quantize_append(caches[r], new_dev[k], slots, pos, after, stream=sh)
+        if timed_idx is not None:
+            m.profile_decode_events(*ev_k[timed_idx])
+        m.decode(caches[r], q, slots, after, max_len, w.scale, out, lse, ws, stream=sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tokens = sum(int(plan[args.warmup + j][4].sum()) for j in range(args.steps))
+    t0 = time.perf_counter()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, sh)
+    for j in range(args.steps):
+        step(args.warmup + j, j)
+    hip.record(e1, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.elapsed_ms(e0, e1)
+    k_ms = [hip.elapsed_ms(a, b) for a, b in ev_k]
+    k_avg_ms = float(np.mean(k_ms))
+    ms_per_step = total_ms / args.steps
+    value = tokens / (total_ms * 1e-3)
+
+    # decode-kernel roofline on the average timed launch
+    alg = [algorithmic(plan[args.warmup + j][4], H, bits) for j in range(args.steps)]
+    by_per_launch = float(np.mean([a[0] for a in alg]))
+    fl_per_launch = float(np.mean([a[1] for a in alg]))
+    gbs = by_per_launch / (k_avg_ms * 1e-3) / 1e9
+    tfs = fl_per_launch / (k_avg_ms * 1e-3) / 1e12
+    t_hbm = by_per_launch / (HBM_PEAK_GBS * 1e9)
+    t_mfma = fl_per_launch / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    traffic = committed_traffic(args.workload)
+    if t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": "C4R4 MLA decode: KV tokens/s and achieved HBM GB/s (% of peak), 128K ctx",
+        "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded generator: c ~ N(0,1) with 8 outlier channels x20, k_r = RoPE(N(0,1)), "
+                "q ~ N(0,1), bf16)",
+        "config": {"workload": w.name, "batch": B, "heads": H, "d_c": 512, "d_r": 64,
+                   "bits": f"C{bits}R4", "context": int(max_len) if w.steps_append == 0 else "log-uniform 1K-128K",
+                   "page_tokens": 64, "sink": 4, "recent": 128, "kv_tokens_per_step": int(tokens / args.steps),
+                   "cache_instances": R, "parallelism": "single GPU"},
+        "hbm_gbps_algorithmic": round(gbs, 1), "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_kernel_ms": round(k_avg_ms, 5), "decode_kernel_ms_p10_p90": [round(float(np.percentile(k_ms, 10)), 5),
+                                                                           round(float(np.percentile(k_ms, 90)), 5)],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "setup_s": round(t_setup, 1), "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

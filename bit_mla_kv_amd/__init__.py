@@ -55,6 +55,8 @@ def _load():
     L.mla_lowbit_decode.restype = ctypes.c_int
     L.mla_lowbit_status_string.argtypes = [ctypes.c_int]
     L.mla_lowbit_status_string.restype = ctypes.c_char_p
+    L.mla_lowbit_profile_decode_events.argtypes = [P, P]
+    L.mla_lowbit_profile_decode_events.restype = ctypes.c_int
     L.mla_lowbit_last_error.argtypes = []
     L.mla_lowbit_last_error.restype = ctypes.c_char_p
     return L
@@ -62,7 +64,8 @@ def _load():
 
 lib = _load()
 EXPORTS = ("mla_lowbit_page_bytes", "mla_lowbit_quantize_append", "mla_lowbit_decode_workspace_bytes",
-           "mla_lowbit_decode", "mla_lowbit_status_string", "mla_lowbit_last_error")
+           "mla_lowbit_decode", "mla_lowbit_profile_decode_events", "mla_lowbit_status_string",
+           "mla_lowbit_last_error")
 
 
 def _check(status: int) -> None:
@@ -125,6 +128,11 @@ def quantize_append(cache: PagedCache, kv_new: torch.Tensor, token_slot: torch.T
     d = cache.desc
     _check(lib.mla_lowbit_quantize_append(ctypes.byref(d), _ptr(kv_new), _ptr(token_slot), _ptr(token_pos),
                                           _ptr(slot_len_after), n, _stream(stream)))
+
+
+def profile_decode_events(start, stop) -> None:
+    """Arm two hipEvent_t handles (ints) around the next decode kernel on this thread."""
+    _check(lib.mla_lowbit_profile_decode_events(start, stop))
 
 
 def decode_workspace_bytes(layout: Layout, batch: int, num_heads: int, max_seq_len: int) -> int:

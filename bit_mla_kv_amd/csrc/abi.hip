@@ -12,6 +12,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -126,9 +127,16 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_
   return ws_layout(batch, num_heads, cfg.n_splits).total;
 }
 
-int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
-                      int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
-                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+int mla_lowbit_profile_decode_events(void* start, void* stop) {
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
+  return MLA_LOWBIT_OK;
+}
+
+static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
+                       int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream, hipEvent_t ev0,
+                       hipEvent_t ev1) {
   int st = check_cache(cache);
   if (st != MLA_LOWBIT_OK) return st;
   if (batch < 0 || max_seq_len < 0)
@@ -175,10 +183,25 @@ int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ev0 && (st = device_status(hipEventRecord(ev0, s), "profile start event")) != MLA_LOWBIT_OK) return st;
   st = device_status(mla::launch_decode(p, cache->layout.bits_c, s), "decode launch");
   if (st != MLA_LOWBIT_OK) return st;
+  if (ev1 && (st = device_status(hipEventRecord(ev1, s), "profile stop event")) != MLA_LOWBIT_OK) return st;
   return device_status(mla::launch_combine(p, s), "combine launch");
 }
+
+int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
+                      int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  return decode_impl(cache, q, seq_slot, seq_len, batch, num_heads, max_seq_len, softmax_scale, out, lse, workspace,
+                     workspace_bytes, stream, ev0, ev1);
+}
+
+}  // extern "C"
+
+extern "C" {
 
 const char* mla_lowbit_status_string(int status) {
   switch (status) {

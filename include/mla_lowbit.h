@@ -167,6 +167,17 @@ int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_
                       int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement aid (not needed for decoding).  Arms two caller-created HIP
+ * events (hipEvent_t passed as void*) for the NEXT mla_lowbit_decode call on
+ * this thread: that call records `start` on its stream immediately before
+ * the split-KV decode kernel and `stop` immediately after it (before the
+ * log-sum-exp combine), so hipEventElapsedTime(start, stop) is that kernel's
+ * duration.  The events are disarmed after that call (also when it fails).
+ * Passing NULL, NULL disarms.  Returns MLA_LOWBIT_OK.
+ */
+int mla_lowbit_profile_decode_events(void* start, void* stop);
+
 /* Static description of a status code. */
 const char* mla_lowbit_status_string(int status);
 
