@@ -68,14 +68,15 @@ int device_status(hipError_t e, const char* what) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t lse_off, o_off, total;
+  size_t ml_off, z_off, o_off, total;
 };
 
 WsLayout ws_layout(int batch, int heads, int n_splits) {
   WsLayout w;
   const size_t rows = (size_t)batch * n_splits * heads;
-  w.lse_off = 0;
-  w.o_off = align_up(rows * sizeof(float), 256);
+  w.ml_off = 0;
+  w.z_off = align_up(rows * 2 * sizeof(float), 256);
+  w.o_off = w.z_off + align_up(rows * 8 * sizeof(float), 256);
   w.total = w.o_off + rows * mla::kDc * sizeof(float);
   return w;
 }
@@ -178,7 +179,9 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.pages_per_split = cfg.pages_per_split;
   p.n_splits = cfg.n_splits;
   p.head_groups = num_heads / cfg.heads_per_wg;
-  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.lse_off);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  p.ws_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.z_off);
+  p.has_z = cfg.heads_per_wg == 128;
   p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;

@@ -31,18 +31,12 @@
 #include <algorithm>
 #include <cstdlib>
 
-#include "mla_internal.h"
+#include "decode_common.h"
 
 namespace mla {
 namespace {
 
-typedef _Float16 f16;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+using namespace dev;
 
 constexpr int kTile = 64;        // tokens per tile (one page)
 constexpr int kStride = 600;     // LDS tile row stride in halves (bank-spread for 16-row reads)
@@ -56,73 +50,6 @@ struct __align__(16) Smem {
   float zr[kTile];                 // RoPE-group zero; 0 for masked tokens
   float bias[kTile];               // 0 valid, -inf masked
 };
-
-__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
-
-// position offset p (0..7) inside an 8-channel block -> channel offset, as the
-// unpacking below orders them (content codes of the layout's width; RoPE codes are 4 bit)
-template <int BITS>
-__device__ __forceinline__ constexpr int perm8(int p) {
-  return BITS == 4 ? ((p & 3) * 2 + (p >> 2)) : ((p & 1) * 4 + (p >> 1));
-}
-
-// 8 nibbles (channels 0..7 of a dword) -> exact fp16 codes in perm8<4> order
-__device__ __forceinline__ uint4 unpack4(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
-  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
-  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
-  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
-  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
-}
-
-// 16 crumbs (channels 0..15 of a dword) -> two groups of 8 exact fp16 codes in perm8<2> order
-__device__ __forceinline__ void unpack2(uint32_t w, uint4& first, uint4& second) {
-  const uint32_t b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;
-  const uint32_t b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
-  first = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 512.0f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 512.0f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 512.0f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b3, 512.0f, false)));
-  second = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 512.0f, true)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 512.0f, true)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 512.0f, true)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b3, 512.0f, true)));
-}
-
-// 8 bf16 values (one 16-byte chunk, channels 0..7) -> fp16 in the order perm8<BITS>
-template <int BITS>
-__device__ __forceinline__ uint4 bf16_chunk_to_f16(uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  f16 h[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = perm8<BITS>(j);
-    const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
-    h[j] = (f16)bf16f(bits);
-  }
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, f16x2{h[0], h[1]});
-  r.y = __builtin_bit_cast(uint32_t, f16x2{h[2], h[3]});
-  r.z = __builtin_bit_cast(uint32_t, f16x2{h[4], h[5]});
-  r.w = __builtin_bit_cast(uint32_t, f16x2{h[6], h[7]});
-  return r;
-}
-
-__device__ __forceinline__ f16x8 lds_read8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
-
-__device__ __forceinline__ f16x4 lds_tr4(const f16* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
-  return __builtin_bit_cast(f16x4, v);
-}
-
-__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float fmax4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
 
 // ---------------------------------------------------------------------------------------
 // BITS_C: content code bits; HB: 16-head blocks per workgroup; TS: waves splitting a tile's tokens.
@@ -509,19 +436,20 @@ __global__ __launch_bounds__(64 * HB * TS) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- write the normalised partial and its log2 lse
+  // ---- write the unnormalised partial with its running max and sum
   const int64_t row = ((int64_t)b * p.n_splits + split) * p.heads + my_head;
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
   float* dst = p.ws_o + row * kDc;
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pos = 16 * cb + 4 * G + i;
-      dst[8 * (pos >> 3) + perm8<BITS_C>(pos & 7)] = O[cb][i] * inv;
+      dst[8 * (pos >> 3) + perm8<BITS_C>(pos & 7)] = O[cb][i];
     }
-  if (G == 0) p.ws_lse[row] = empty ? -__builtin_inff() : M + __log2f(l_tot);
+  if (G == 0) {
+    p.ws_ml[2 * row] = M;
+    p.ws_ml[2 * row + 1] = l_tot;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -546,20 +474,27 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
   const int64_t base = (int64_t)b * p.n_splits * p.heads + h;  // row of split s: base + s*heads
 
   float M = -__builtin_inff();
-  for (int s = 0; s < nvs; ++s) M = fmaxf(M, p.ws_lse[base + (int64_t)s * p.heads]);
+  for (int s = 0; s < nvs; ++s) {
+    const int64_t row = base + (int64_t)s * p.heads;
+    if (p.ws_ml[2 * row + 1] > 0.f) M = fmaxf(M, p.ws_ml[2 * row]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = -__builtin_inff();
   if (M != -__builtin_inff()) {
-    float sum = 0.f;
-    for (int s = 0; s < nvs; ++s) sum += __builtin_amdgcn_exp2f(p.ws_lse[base + (int64_t)s * p.heads] - M);
-    L = M + __log2f(sum);
+    float den = 0.f;
+    const int g = t / 16;  // channels 4t..4t+3 lie in group t/16
     for (int s = 0; s < nvs; ++s) {
       const int64_t row = base + (int64_t)s * p.heads;
-      const float wgt = __builtin_amdgcn_exp2f(p.ws_lse[row] - L);
-      if (wgt == 0.f) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
+      const float l = p.ws_ml[2 * row + 1];
+      if (!(l > 0.f)) continue;
+      const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * row] - M);
+      den += wgt * l;
+      f32x4 v = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
+      if (p.has_z) v += p.ws_z[row * 8 + g];
       acc += wgt * v;
     }
+    acc *= 1.f / den;
+    L = M + __log2f(den);
   }
   uint16_t* o = p.out + ((int64_t)b * p.heads + h) * kDc + 4 * t;
   uint2 packed;
@@ -590,8 +525,10 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
     cfg->heads_per_wg = 16; cfg->threads = 128; cfg->wg_per_cu = 2;
   } else if (heads == 32) {
     cfg->heads_per_wg = 32; cfg->threads = 256; cfg->wg_per_cu = 1;
-  } else if (heads > 0 && heads % 64 == 0) {
+  } else if (heads == 64) {
     cfg->heads_per_wg = 64; cfg->threads = 256; cfg->wg_per_cu = 1;
+  } else if (heads > 0 && heads % 128 == 0) {
+    cfg->heads_per_wg = 128; cfg->threads = 256; cfg->wg_per_cu = 1;
   } else {
     return false;
   }
@@ -617,6 +554,7 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
 
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream) {
   const int hpw = p.heads / p.head_groups;
+  if (hpw == 128) return launch_decode128(p, bits_c, stream);
   if (bits_c == 4) {
     if (hpw == 16) return launch_t<4, 1, 2>(p, stream);
     if (hpw == 32) return launch_t<4, 2, 2>(p, stream);

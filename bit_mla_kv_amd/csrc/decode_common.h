@@ -1,0 +1,107 @@
+// Device helpers shared by the decode kernels (gfx950).
+#pragma once
+#include "mla_internal.h"
+
+namespace mla {
+namespace dev {
+
+typedef _Float16 f16;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// position offset p (0..7) inside an 8-channel block -> channel offset, as the
+// unpacking below orders them (content codes of the layout's width; RoPE codes are 4 bit)
+template <int BITS>
+__device__ __forceinline__ constexpr int perm8(int p) {
+  return BITS == 4 ? ((p & 3) * 2 + (p >> 2)) : ((p & 1) * 4 + (p >> 1));
+}
+
+// 8 nibbles (channels 0..7 of a dword) -> exact fp16 codes in perm8<4> order
+__device__ __forceinline__ uint4 unpack4(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
+// 16 crumbs (channels 0..15 of a dword) -> two groups of 8 exact fp16 codes in perm8<2> order
+__device__ __forceinline__ void unpack2(uint32_t w, uint4& first, uint4& second) {
+  const uint32_t b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;
+  const uint32_t b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  first = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 512.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 512.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 512.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b3, 512.0f, false)));
+  second = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 512.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 512.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b2, 512.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b3, 512.0f, true)));
+}
+
+// 8 bf16 values (one 16-byte chunk, channels 0..7) -> fp16 in the order perm8<BITS>
+template <int BITS>
+__device__ __forceinline__ uint4 bf16_chunk_to_f16(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  f16 h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = perm8<BITS>(j);
+    const uint32_t bits = (c & 1) ? (w[c >> 1] >> 16) : (w[c >> 1] & 0xFFFFu);
+    h[j] = (f16)bf16f(bits);
+  }
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, f16x2{h[0], h[1]});
+  r.y = __builtin_bit_cast(uint32_t, f16x2{h[2], h[3]});
+  r.z = __builtin_bit_cast(uint32_t, f16x2{h[4], h[5]});
+  r.w = __builtin_bit_cast(uint32_t, f16x2{h[6], h[7]});
+  return r;
+}
+
+__device__ __forceinline__ f16x8 lds_read8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// Explicit LDS (address space 3) pointers.  An LDS address can be passed through an empty asm
+// statement (to keep address arithmetic from being hoisted out of a loop) without losing its
+// address space, which a generic pointer would (turning ds_read into flat loads).
+template <typename T>
+using lds_ptr = __attribute__((address_space(3))) T*;
+
+template <typename T>
+__device__ __forceinline__ lds_ptr<T> lds_opaque(T* generic) {
+  uint32_t off = (uint32_t)reinterpret_cast<uintptr_t>(generic);  // low bits of a generic LDS address
+  asm volatile("" : "+v"(off));
+  return reinterpret_cast<lds_ptr<T>>(static_cast<uintptr_t>(off));
+}
+
+template <typename T, typename P>
+__device__ __forceinline__ T lds_load(lds_ptr<P> p) {
+  return *reinterpret_cast<lds_ptr<const T>>(p);
+}
+
+__device__ __forceinline__ f16x4 lds_tr4(const f16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+__device__ __forceinline__ f16x4 lds_tr4(lds_ptr<f16> p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_ptr<i16x4>>(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fmax4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+}  // namespace dev
+}  // namespace mla

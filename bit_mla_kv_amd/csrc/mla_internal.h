@@ -51,8 +51,10 @@ struct DecodeParams {
   int32_t pages_per_split;
   int32_t n_splits;           // per sequence: 1 bf16 split + packed splits
   int32_t head_groups;        // heads / heads-per-workgroup
-  float* ws_o;                // [batch][n_splits][H][512], normalised partial outputs
-  float* ws_lse;              // [batch][n_splits][H], log2-domain partial lse (-inf: empty)
+  float* ws_o;                // [batch][n_splits][H][512]: unnormalised partial outputs sum_t 2^(x_t - m) v_t
+  float* ws_ml;               // [batch][n_splits][H][2]: running max m (log2 domain) and sum l (l = 0: empty)
+  float* ws_z;                // [batch][n_splits][H][8]: zero-term sums sum_t 2^(x_t - m) z_t,g (has_z)
+  int32_t has_z;              // ws_z holds zero terms still to be added to each group's channels
   uint16_t* out;              // [batch][H][512] bf16
   float* lse;                 // [batch][H] natural log, may be null
 };
@@ -60,6 +62,7 @@ struct DecodeParams {
 // Kernel launchers (each returns the hipError_t of its launch).
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream);
+hipError_t launch_decode128(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 
 // Decode configuration shared by the workspace query and the launch.
