@@ -26,6 +26,7 @@ UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
     "decode128.hip": [],
+    "plan.hip": [],
     "abi.hip": [],
 }
 

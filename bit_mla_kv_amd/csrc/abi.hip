@@ -68,14 +68,17 @@ int device_status(hipError_t e, const char* what) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t ml_off, z_off, o_off, total;
+  size_t hdr_off, items_off, seq_off, ml_off, z_off, o_off, total;
 };
 
-WsLayout ws_layout(int batch, int heads, int n_splits) {
+WsLayout ws_layout(int batch, int heads, int max_items) {
   WsLayout w;
-  const size_t rows = (size_t)batch * n_splits * heads;
-  w.ml_off = 0;
-  w.z_off = align_up(rows * 2 * sizeof(float), 256);
+  const size_t rows = (size_t)max_items * heads;
+  w.hdr_off = 0;
+  w.items_off = 256;
+  w.seq_off = w.items_off + align_up((size_t)max_items * 16, 256);
+  w.ml_off = w.seq_off + align_up((size_t)batch * 16, 256);
+  w.z_off = w.ml_off + align_up(rows * 2 * sizeof(float), 256);
   w.o_off = w.z_off + align_up(rows * 8 * sizeof(float), 256);
   w.total = w.o_off + rows * mla::kDc * sizeof(float);
   return w;
@@ -125,7 +128,7 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_
   if (check_layout(layout) != MLA_LOWBIT_OK || batch < 0 || max_seq_len < 0) return 0;
   mla::DecodeConfig cfg;
   if (!mla::decode_config(num_heads, layout->n_sink, layout->n_recent, batch, max_seq_len, &cfg)) return 0;
-  return ws_layout(batch, num_heads, cfg.n_splits).total;
+  return ws_layout(batch, num_heads, cfg.max_items).total;
 }
 
 int mla_lowbit_profile_decode_events(void* start, void* stop) {
@@ -153,7 +156,7 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
     return fail(MLA_LOWBIT_ERR_INVALID_ARG, "out must be a 16-byte aligned device pointer");
   if (!seq_slot || !seq_len) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "seq_slot and seq_len must be non-NULL");
   if (lse && !aligned(lse, 4)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const WsLayout wl = ws_layout(batch, num_heads, cfg.n_splits);
+  const WsLayout wl = ws_layout(batch, num_heads, cfg.max_items);
   if (!workspace || !aligned(workspace, 256))
     return fail(MLA_LOWBIT_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device pointer");
   if (workspace_bytes < wl.total)
@@ -176,9 +179,15 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.batch = batch;
   p.heads = num_heads;
   p.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
-  p.pages_per_split = cfg.pages_per_split;
-  p.n_splits = cfg.n_splits;
   p.head_groups = num_heads / cfg.heads_per_wg;
+  p.target_items = cfg.target_items;
+  p.min_pages_per_split = cfg.min_pages_per_split;
+  p.force_pages_per_split = cfg.force_pages_per_split;
+  p.max_items = cfg.max_items;
+  char* wsb = static_cast<char*>(workspace);
+  p.plan_hdr = reinterpret_cast<int32_t*>(wsb + wl.hdr_off);
+  p.items = reinterpret_cast<int32_t*>(wsb + wl.items_off);
+  p.seq_info = reinterpret_cast<int32_t*>(wsb + wl.seq_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
   p.ws_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.z_off);
   p.has_z = cfg.heads_per_wg == 128;
@@ -186,6 +195,8 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = device_status(mla::launch_plan(p, s), "plan launch");
+  if (st != MLA_LOWBIT_OK) return st;
   if (ev0 && (st = device_status(hipEventRecord(ev0, s), "profile start event")) != MLA_LOWBIT_OK) return st;
   st = device_status(mla::launch_decode(p, cache->layout.bits_c, s), "decode launch");
   if (st != MLA_LOWBIT_OK) return st;

@@ -84,10 +84,11 @@ __global__ __launch_bounds__(64 * HB * TS) void decode_kernel(DecodeParams p) {
   // and share its L2 for the page stream.
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int hg = kx % p.head_groups;
-  const int pair = xcd + 8 * (kx / p.head_groups);
-  if (pair >= p.batch * p.n_splits) return;
-  const int split = pair % p.n_splits;
-  const int b = pair / p.n_splits;
+  const int item = xcd + 8 * (kx / p.head_groups);
+  if (item >= min(p.plan_hdr[0], p.max_items)) return;
+  const int4 itm = reinterpret_cast<const int4*>(p.items)[item];
+  const int b = itm.x;
+  const int split = itm.w ? 0 : 1;  // 0: bf16 tokens, otherwise a packed chunk
 
   int N = p.seq_len[b];
   const int slot = p.seq_slot[b];
@@ -107,10 +108,9 @@ __global__ __launch_bounds__(64 * HB * TS) void decode_kernel(DecodeParams p) {
     nb = ns + max(0, N - rstart);
     n_iter = (nb + kTile - 1) / kTile;
   } else {
-    page0 = first_page + (split - 1) * p.pages_per_split;
-    const int page_end = min(first_page + split * p.pages_per_split, first_page + n_pp);
-    n_iter = page_end - page0;
-    if (n_iter <= 0) return;  // beyond this sequence: combine ignores the split
+    page0 = itm.y;
+    n_iter = min(itm.z, first_page + n_pp - page0);
+    if (n_iter <= 0) return;
   }
 
   const int head_base = hg * 16 * HB + hb * 16;
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(64 * HB * TS) void decode_kernel(DecodeParams p) {
   }
 
   // ---- write the unnormalised partial with its running max and sum
-  const int64_t row = ((int64_t)b * p.n_splits + split) * p.heads + my_head;
+  const int64_t row = (int64_t)item * p.heads + my_head;
   float* dst = p.ws_o + row * kDc;
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb)
@@ -452,58 +452,6 @@ __global__ __launch_bounds__(64 * HB * TS) void decode_kernel(DecodeParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// LSE combine: one workgroup per (sequence, head), 128 threads x 4 channels.
-__device__ __forceinline__ uint16_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
-  const int b = blockIdx.x / p.heads;
-  const int h = blockIdx.x % p.heads;
-  const int t = threadIdx.x;
-  int N = p.seq_len[b];
-  const int slot = p.seq_slot[b];
-  if (slot < 0 || slot >= p.num_slots) N = 0;
-  const int p_lo = p.n_sink, p_hi = N - p.n_recent;
-  const int first_page = p_lo / kPageTokens;
-  const int n_pp = p_hi > p_lo ? (p_hi - 1) / kPageTokens - first_page + 1 : 0;
-  const int nvs = min(p.n_splits, 1 + (n_pp + p.pages_per_split - 1) / p.pages_per_split);
-  const int64_t base = (int64_t)b * p.n_splits * p.heads + h;  // row of split s: base + s*heads
-
-  float M = -__builtin_inff();
-  for (int s = 0; s < nvs; ++s) {
-    const int64_t row = base + (int64_t)s * p.heads;
-    if (p.ws_ml[2 * row + 1] > 0.f) M = fmaxf(M, p.ws_ml[2 * row]);
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = -__builtin_inff();
-  if (M != -__builtin_inff()) {
-    float den = 0.f;
-    const int g = t / 16;  // channels 4t..4t+3 lie in group t/16
-    for (int s = 0; s < nvs; ++s) {
-      const int64_t row = base + (int64_t)s * p.heads;
-      const float l = p.ws_ml[2 * row + 1];
-      if (!(l > 0.f)) continue;
-      const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * row] - M);
-      den += wgt * l;
-      f32x4 v = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
-      if (p.has_z) v += p.ws_z[row * 8 + g];
-      acc += wgt * v;
-    }
-    acc *= 1.f / den;
-    L = M + __log2f(den);
-  }
-  uint16_t* o = p.out + ((int64_t)b * p.heads + h) * kDc + 4 * t;
-  uint2 packed;
-  packed.x = (uint32_t)f2bf_rne(acc[0]) | ((uint32_t)f2bf_rne(acc[1]) << 16);
-  packed.y = (uint32_t)f2bf_rne(acc[2]) | ((uint32_t)f2bf_rne(acc[3]) << 16);
-  *reinterpret_cast<uint2*>(o) = packed;
-  if (p.lse && t == 0) p.lse[(int64_t)b * p.heads + h] = L * 0.69314718055994531f;
-}
-
 template <int BITS_C, int HB, int TS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const size_t smem = sizeof(Smem);
@@ -511,8 +459,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  const int64_t pairs = (int64_t)p.batch * p.n_splits;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * p.head_groups;
+  const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * HB * TS), smem, stream, p);
   return hipGetLastError();
 }
@@ -528,7 +475,7 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
   } else if (heads == 64) {
     cfg->heads_per_wg = 64; cfg->threads = 256; cfg->wg_per_cu = 1;
   } else if (heads > 0 && heads % 128 == 0) {
-    cfg->heads_per_wg = 128; cfg->threads = 256; cfg->wg_per_cu = 1;
+    cfg->heads_per_wg = 128; cfg->threads = 512; cfg->wg_per_cu = 1;
   } else {
     return false;
   }
@@ -538,17 +485,27 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) num_cu = v;
   }
-  const int64_t max_pp = std::max<int64_t>(0, ((int64_t)max_seq_len - n_recent + kPageTokens - 1) / kPageTokens);
   const int64_t head_groups = heads / cfg->heads_per_wg;
-  const int64_t slots = (int64_t)num_cu * cfg->wg_per_cu;
-  int64_t pps = (batch * max_pp * head_groups + slots - 1) / std::max<int64_t>(1, slots);
-  pps = std::max<int64_t>(pps, 4);
+  int64_t target = std::max<int64_t>(1, (int64_t)num_cu * cfg->wg_per_cu / head_groups);
+  if (const char* env = getenv("MLA_LOWBIT_TARGET_ITEMS")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v > 0) target = v;
+  }
+  cfg->target_items = (int)std::min<int64_t>(target, 1 << 20);
+  cfg->min_pages_per_split = 4;
+  cfg->force_pages_per_split = 0;
   if (const char* env = getenv("MLA_LOWBIT_PAGES_PER_SPLIT")) {
     const long v = strtol(env, nullptr, 10);
-    if (v > 0) pps = v;
+    if (v > 0) cfg->force_pages_per_split = (int)std::min<long>(v, 1 << 20);
   }
-  cfg->pages_per_split = (int)std::min<int64_t>(pps, 1 << 20);
-  cfg->n_splits = 1 + (int)((max_pp + pps - 1) / pps);
+  const int64_t max_pp = std::max<int64_t>(0, ((int64_t)max_seq_len - n_recent + kPageTokens - 1) / kPageTokens);
+  int64_t packed_items;
+  if (cfg->force_pages_per_split > 0)
+    packed_items = (int64_t)batch * ((max_pp + cfg->force_pages_per_split - 1) / cfg->force_pages_per_split);
+  else  // full chunks <= total / chunk <= target, plus at most one tail chunk per sequence
+    packed_items = std::min<int64_t>((int64_t)batch * ((max_pp + cfg->min_pages_per_split - 1) / cfg->min_pages_per_split),
+                                     cfg->target_items + (int64_t)batch);
+  cfg->max_items = (int)std::min<int64_t>(packed_items + batch, 1 << 30);
   return true;
 }
 
@@ -567,11 +524,5 @@ hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.batch * p.heads;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(128), 0, stream, p);
-  return hipGetLastError();
-}
 
 }  // namespace mla

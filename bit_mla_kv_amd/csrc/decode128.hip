@@ -86,10 +86,11 @@ __global__ __launch_bounds__(512) void decode128_kernel(DecodeParams p) {
 
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int hg = kx % p.head_groups;
-  const int pair = xcd + 8 * (kx / p.head_groups);
-  if (pair >= p.batch * p.n_splits) return;
-  const int split = pair % p.n_splits;
-  const int b = pair / p.n_splits;
+  const int item = xcd + 8 * (kx / p.head_groups);
+  if (item >= min(p.plan_hdr[0], p.max_items)) return;
+  const int4 itm = reinterpret_cast<const int4*>(p.items)[item];
+  const int b = itm.x;
+  const int split = itm.w ? 0 : 1;  // 0: bf16 tokens, otherwise a packed chunk
 
   int N = p.seq_len[b];
   const int slot = p.seq_slot[b];
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(512) void decode128_kernel(DecodeParams p) {
     nb = ns + max(0, N - rstart);
     n_iter = (nb + kT - 1) / kT;
   } else {
-    page0 = first_page + (split - 1) * p.pages_per_split;
-    n_iter = min(first_page + split * p.pages_per_split, first_page + n_pp) - page0;
+    page0 = itm.y;
+    n_iter = min(itm.z, first_page + n_pp - page0);
     if (n_iter <= 0) return;
   }
 
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(512) void decode128_kernel(DecodeParams p) {
   }
 
   // ---- unnormalised partial: O (PV role), running max / sum and zero-term sums (QK role)
-  const int64_t rows = (int64_t)b * p.n_splits + split;
+  const int64_t rows = item;
   float* dst_o = p.ws_o + rows * p.heads * kDc;
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
@@ -433,8 +434,7 @@ hipError_t launch128(const DecodeParams& p, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  const int64_t pairs = (int64_t)p.batch * p.n_splits;
-  const int64_t blocks = (pairs + 7) / 8 * 8 * p.head_groups;
+  const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), smem, stream, p);
   return hipGetLastError();
 }

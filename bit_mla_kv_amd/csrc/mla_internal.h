@@ -48,12 +48,18 @@ struct DecodeParams {
   const int32_t* seq_len;
   int32_t batch, heads;
   float scale_log2e;          // softmax_scale * log2(e)
-  int32_t pages_per_split;
-  int32_t n_splits;           // per sequence: 1 bf16 split + packed splits
   int32_t head_groups;        // heads / heads-per-workgroup
-  float* ws_o;                // [batch][n_splits][H][512]: unnormalised partial outputs sum_t 2^(x_t - m) v_t
-  float* ws_ml;               // [batch][n_splits][H][2]: running max m (log2 domain) and sum l (l = 0: empty)
-  float* ws_z;                // [batch][n_splits][H][8]: zero-term sums sum_t 2^(x_t - m) z_t,g (has_z)
+  // split plan (written on the device by plan_kernel)
+  int32_t target_items;       // aimed-at number of packed work items (about one per resident workgroup)
+  int32_t min_pages_per_split;
+  int32_t force_pages_per_split;  // > 0: fixed chunk size (tests / tuning)
+  int32_t max_items;          // capacity of items / partial rows
+  int32_t* items;             // [max_items] int4 (sequence, first page, pages, kind 0 packed / 1 bf16)
+  int32_t* seq_info;          // [batch] int4 (first full item, full items, tail item or -1, bf16 item)
+  int32_t* plan_hdr;          // [0] item count, [1] pages per chunk
+  float* ws_o;                // [max_items][H][512]: unnormalised partial outputs sum_t 2^(x_t - m) v_t
+  float* ws_ml;               // [max_items][H][2]: running max m (log2 domain) and sum l (l = 0: empty)
+  float* ws_z;                // [max_items][H][8]: zero-term sums sum_t 2^(x_t - m) z_t,g (has_z)
   int32_t has_z;              // ws_z holds zero terms still to be added to each group's channels
   uint16_t* out;              // [batch][H][512] bf16
   float* lse;                 // [batch][H] natural log, may be null
@@ -63,6 +69,7 @@ struct DecodeParams {
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_decode128(const DecodeParams& p, int bits_c, hipStream_t stream);
+hipError_t launch_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 
 // Decode configuration shared by the workspace query and the launch.
@@ -70,8 +77,10 @@ struct DecodeConfig {
   int heads_per_wg;      // heads covered by one workgroup
   int threads;           // workgroup size
   int wg_per_cu;         // expected resident workgroups per CU
-  int pages_per_split;
-  int n_splits;          // 1 (bf16 tokens) + ceil(max packed pages / pages_per_split)
+  int target_items;      // packed work items the plan aims at
+  int min_pages_per_split;
+  int force_pages_per_split;
+  int max_items;         // bound on plan items (workspace rows, grid)
 };
 bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_len, DecodeConfig* cfg);
 
