@@ -42,8 +42,8 @@ struct Geo {
   static constexpr int PB = kPageTokens * (CB + kDr / 2 + 4 * kGroups);
   static constexpr int UCH = PB / 16;                            // 16-byte chunks per page
   static constexpr int UC = kPageTokens * CB / 16;               // content chunks
-  static constexpr int UPR = CB / 16;                            // content chunks per token row
-  static constexpr int CPT = UC / 512;                           // content chunks per thread
+  static constexpr int CDW = kPageTokens * CB / 4;               // content dwords
+  static constexpr int DPR = CB / 4;                             // content dwords per token row
   static constexpr int META = kPageTokens * (CB + kDr / 2);      // metadata byte offset
 };
 
@@ -213,31 +213,21 @@ __global__ __launch_bounds__(512) void decode128_kernel(DecodeParams p) {
         *reinterpret_cast<uint4*>(&sm.tile[r * kS + kZ]) = make_uint4(0, 0, 0, 0);
       }
     } else {
-#pragma unroll
-      for (int k = 0; k < GE::CPT; ++k) {
+      // content codes, one packed dword per lane and step: consecutive lanes write consecutive
+      // 16-byte (C4) or 32-byte (C2) runs of the tile, which keeps the LDS writes conflict-free
+#pragma unroll 4
+      for (int k = 0; k < GE::CDW / 512; ++k) {
         const int u = tid + k * 512;
-        const uint4 v = *reinterpret_cast<const uint4*>(sm.stage + 16 * u);
-        const int r = u / GE::UPR, ch = u % GE::UPR;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(sm.stage + 4 * u);
+        const int r = u / GE::DPR, d = u % GE::DPR;
         f16* dst = &sm.tile[r * kS];
         if (BITS_C == 4) {
-          *reinterpret_cast<uint4*>(dst + 32 * ch + 0) = unpack4(v.x);
-          *reinterpret_cast<uint4*>(dst + 32 * ch + 8) = unpack4(v.y);
-          *reinterpret_cast<uint4*>(dst + 32 * ch + 16) = unpack4(v.z);
-          *reinterpret_cast<uint4*>(dst + 32 * ch + 24) = unpack4(v.w);
+          *reinterpret_cast<uint4*>(dst + 8 * d) = unpack4(v);
         } else {
           uint4 x0, x1;
-          unpack2(v.x, x0, x1);
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 0) = x0;
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 8) = x1;
-          unpack2(v.y, x0, x1);
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 16) = x0;
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 24) = x1;
-          unpack2(v.z, x0, x1);
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 32) = x0;
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 40) = x1;
-          unpack2(v.w, x0, x1);
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 48) = x0;
-          *reinterpret_cast<uint4*>(dst + 64 * ch + 56) = x1;
+          unpack2(v, x0, x1);
+          *reinterpret_cast<uint4*>(dst + 16 * d) = x0;
+          *reinterpret_cast<uint4*>(dst + 16 * d + 8) = x1;
         }
       }
       if (tid < 128) {  // RoPE-key codes: token tid/2, channels 32*(tid&1) .. +31
@@ -290,25 +280,32 @@ __global__ __launch_bounds__(512) void decode128_kernel(DecodeParams p) {
         const lds_ptr<float> zp = lds_opaque(&sm.zr[0]);
         const lds_ptr<float> bp = lds_opaque(&sm.bias[0]);
         const lds_ptr<f16x8> qf = lds_opaque(&sm.qfrag[0][w][lane]);
+        // the two 16-token blocks form two independent MFMA chains per group
+        const lds_ptr<f16> arow0 = tb + (r0 + L16) * kS + 8 * G;
+        const lds_ptr<f16> arow1 = arow0 + 16 * kS;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          const f16x8 q0 = g < 8 ? qreg[2 * g] : lds_load<f16x8>(qf);
+          const f16x8 q1 = g < 8 ? qreg[2 * g + 1] : lds_load<f16x8>(qf + 8 * 64);
+          const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+          f32x4 c0 = mfma16(lds_load<f16x8>(arow0 + 64 * g), q0, z4);
+          f32x4 c1 = mfma16(lds_load<f16x8>(arow1 + 64 * g), q0, z4);
+          c0 = mfma16(lds_load<f16x8>(arow0 + 64 * g + 32), q1, c0);
+          c1 = mfma16(lds_load<f16x8>(arow1 + 64 * g + 32), q1, c1);
+          const f32x4 sc0 = lds_load<f32x4>(sq + g * kT + r0 + 4 * G);
+          const f32x4 sc1 = lds_load<f32x4>(sq + g * kT + r0 + 16 + 4 * G);
+          s0 += sc0 * c0;
+          s1 += sc1 * c1;
+        }
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
-          const lds_ptr<f16> arow = tb + (r0 + 16 * bk + L16) * kS + 8 * G;
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int g = 0; g < kGroups; ++g) {
-            const f16x8 q0 = g < 8 ? qreg[2 * g] : lds_load<f16x8>(qf);
-            const f16x8 q1 = g < 8 ? qreg[2 * g + 1] : lds_load<f16x8>(qf + 8 * 64);
-            f32x4 acc = mfma16(lds_load<f16x8>(arow + 64 * g), q0, f32x4{0.f, 0.f, 0.f, 0.f});
-            acc = mfma16(lds_load<f16x8>(arow + 64 * g + 32), q1, acc);
-            const f32x4 sc = lds_load<f32x4>(sq + g * kT + r0 + 16 * bk + 4 * G);
-            s += sc * acc;
-          }
           // zero terms of the content groups: every lane reads z_0..z_7 (B: hi / lo parts of qsum)
           const lds_ptr<f16> zrow = tb + (r0 + 16 * bk + L16) * kS + kZ;
           const f32x4 accz = mfma16(lds_load<f16x8>(zrow), lds_load<f16x8>(qf + 16 * 64), f32x4{0.f, 0.f, 0.f, 0.f});
           const f32x4 zv = lds_load<f32x4>(zp + r0 + 16 * bk + 4 * G);
           const f32x4 bv = lds_load<f32x4>(bp + r0 + 16 * bk + 4 * G);
-          S[bk] = s + accz + zv * qr8 + bv;
+          S[bk] = (bk == 0 ? s0 : s1) + accz + zv * qr8 + bv;
         }
       }
       // online softmax for the 16 heads (log2 domain, lazy max refresh)
