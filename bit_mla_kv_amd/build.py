@@ -25,7 +25,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
-    "decode128.hip": [],
+    "decode64.hip": [],
     "plan.hip": [],
     "abi.hip": [],
 }

@@ -190,7 +190,7 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.seq_info = reinterpret_cast<int32_t*>(wsb + wl.seq_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
   p.ws_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.z_off);
-  p.has_z = cfg.heads_per_wg == 128;
+  p.has_z = cfg.heads_per_wg == 64;  // the 64-head kernel leaves the zero-term sums to the combine
   p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;

@@ -472,10 +472,8 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
     cfg->heads_per_wg = 16; cfg->threads = 128; cfg->wg_per_cu = 2;
   } else if (heads == 32) {
     cfg->heads_per_wg = 32; cfg->threads = 256; cfg->wg_per_cu = 1;
-  } else if (heads == 64) {
-    cfg->heads_per_wg = 64; cfg->threads = 256; cfg->wg_per_cu = 1;
-  } else if (heads > 0 && heads % 128 == 0) {
-    cfg->heads_per_wg = 128; cfg->threads = 512; cfg->wg_per_cu = 1;
+  } else if (heads > 0 && heads % 64 == 0) {
+    cfg->heads_per_wg = 64; cfg->threads = 512; cfg->wg_per_cu = 1;
   } else {
     return false;
   }
@@ -511,7 +509,7 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
 
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream) {
   const int hpw = p.heads / p.head_groups;
-  if (hpw == 128) return launch_decode128(p, bits_c, stream);
+  if (hpw == 64) return launch_decode64(p, bits_c, stream);
   if (bits_c == 4) {
     if (hpw == 16) return launch_t<4, 1, 2>(p, stream);
     if (hpw == 32) return launch_t<4, 2, 2>(p, stream);

@@ -1,0 +1,588 @@
+// Split-KV low-bit MLA decode for groups of 64 query heads on gfx950 (CDNA4).
+//
+// Same computation as decode.hip (QuantMLA pages: ai.info summary, "Key
+// Contributions", item 4; onedev.kr review, "How it is used"): one global
+// softmax over all valid tokens, sink / recent tokens from bf16, all others
+// from their packed copies, output aggregated over the content latent.
+//
+// One workgroup of 8 waves per (sequence, split, 64-head group), specialised
+// by role so that each wave keeps only its own long-lived registers.  The
+// shared LDS read bandwidth (128 B/clk/CU) is the binding resource, so the
+// roles are cut to keep LDS bytes per token low:
+//  - QK waves 0, 1 hold the queries of 32 heads each and score one 32-token
+//    tile per step with MFMA 16x16x32 f16 (queries as the A operand, so each
+//    lane owns one token of a 16-token block and applies that token's fp32
+//    group scales as scalars; every tile operand read feeds two head blocks).
+//    The zero terms of all nine groups go through one more MFMA against the
+//    tile's zero columns with qsum split into fp16 hi + lo.  Online softmax in
+//    the log2 domain with a lazily refreshed running max; probabilities are
+//    published to LDS as fp16 [token][head];
+//  - unpack waves 2, 3 load the packed bytes of a tile from HBM into
+//    registers three steps ahead and unpack them into an fp16 tile of exact
+//    codes (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
+//    converted with a 2^9 scale) plus per-token scales, zeros and masks;
+//  - PV waves 4..7 hold the output of content groups 2v, 2v+1 (v = w - 4) for
+//    all 64 heads and accumulate p * s_g times the exact codes (MFMA 32x32x16
+//    f16, both operands read with the LDS transpose load) plus the zero-term
+//    sums sum_t p_t z_g,t.
+// Tiles flow through a three-slot LDS ring: in step k the QK waves score tile
+// k, the PV waves accumulate tile k - 1 and the unpack waves write tile k + 1;
+// one workgroup barrier per tile.
+// Partials are left unnormalised with their running max and sum; the combine
+// kernel adds the zero terms and merges splits.
+#include <algorithm>
+
+#include "decode_common.h"
+
+namespace mla {
+namespace {
+using namespace dev;
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kT = 32;            // tokens per tile (half a page)
+constexpr int kHW = 64;           // query heads per workgroup
+constexpr int kThreads = 512;     // 2 QK waves, 2 unpack waves, 4 PV waves
+constexpr int kSlots = 3;         // tile ring
+constexpr int kS = 592;           // tile row stride (halves): 576 codes + 16 zero-term columns
+constexpr int kZ = 576;           // zero-term columns: z_0..z_7, then z_8 and seven zeros
+constexpr int kPT = 72;           // probability row stride (halves); rows are tokens
+constexpr float kRescale = 8.0f;  // lazy max refresh threshold, log2 units
+
+template <int BITS_C>
+struct Geo {
+  static constexpr int CB = kDc * BITS_C / 8;                              // content bytes per token
+  static constexpr int PB = kPageTokens * (CB + kDr / 2 + 4 * kGroups);   // page bytes
+  static constexpr int ROPE0 = kPageTokens * CB;                           // RoPE block of a page
+  static constexpr int META0 = kPageTokens * (CB + kDr / 2);               // metadata block of a page
+  static constexpr int CDW = kT * CB / 4;      // content dwords of a tile
+  static constexpr int DPR = CB / 4;           // content dwords per token
+  static constexpr int CPT = CDW / 128;        // content dwords per unpack thread
+  static constexpr int RPT = kT * kDr / 8 / 128;  // RoPE dwords per unpack thread (2)
+  static_assert(CDW % 128 == 0 && RPT == 2, "unpack split assumes these sizes");
+};
+
+// packed bytes of one tile held by an unpack thread (wave 2 lanes < 32 also carry one token's metadata)
+template <int BITS_C>
+struct TileRegs {
+  uint32_t c[Geo<BITS_C>::CPT];
+  uint32_t r[2];
+  uint3 m[3];
+};
+
+template <int BITS_C>
+struct __align__(16) Smem64 {
+  f16 tile[kSlots][kT * kS];       // exact codes of a tile's tokens + zero-term columns
+  f16 probT[2][kT][kPT];           // fp16 probabilities [token][head] of steps k (QK) and k - 1 (PV)
+  float sq[kSlots][kGroups][kT];   // s_g * scale * log2 e at sq_pos(token); 0 for masked tokens
+  float bias[kSlots][kT];          // at sq_pos(token): 0 valid, -inf masked
+  f16 svh[kSlots][8][kT];          // PV group scale s_g (fp16); 0 for masked tokens
+  float alpha[2][kHW];             // per-head rescale factor for the PV accumulators
+  int resc[2][2];                  // per-QK-wave "some head was rescaled" flags
+  f16x8 qfrag[3][2][2][64];        // [RoPE step 0, RoPE step 1, zero-term step][QK wave][head block][lane]
+};
+
+// Per-token QK constants sit so that one 8-byte read gives a lane the values of its token in
+// both 16-token blocks: token r at 2 * (r % 16) + r / 16.
+__device__ __forceinline__ int sq_pos(int r) { return 2 * (r & 15) + (r >> 4); }
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// max / sum over the 16 lanes of a row (lanes 16k .. 16k + 15)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 64));
+  v = fmaxf(v, __shfl_xor(v, 2, 64));
+  v = fmaxf(v, __shfl_xor(v, 4, 64));
+  return fmaxf(v, __shfl_xor(v, 8, 64));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  return v + __shfl_xor(v, 8, 64);
+}
+
+// Scalar (SMEM) read of a wave-uniform int: it counts on lgkmcnt, so waiting for it leaves the
+// vector loads of staged tiles in flight.
+__device__ __forceinline__ int scalar_load(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+template <int BITS_C>
+__global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
+  using GE = Geo<BITS_C>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem64<BITS_C>& sm = *reinterpret_cast<Smem64<BITS_C>*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar: roles branch uniformly
+  const int G = lane >> 4;       // 16x16x32 k slice / D row block
+  const int L16 = lane & 15;
+  const int half = lane >> 5;    // 32x32x16 k half
+  const int l32 = lane & 31;
+
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int hg = kx % p.head_groups;
+  const int item = xcd + 8 * (kx / p.head_groups);
+  if (item >= min(p.plan_hdr[0], p.max_items)) return;
+  const int4 itm = reinterpret_cast<const int4*>(p.items)[item];
+  const int b = itm.x;
+  const bool packed = itm.w == 0;  // otherwise the item holds the sequence's bf16 tokens
+
+  int N = p.seq_len[b];
+  const int slot = p.seq_slot[b];
+  if (slot < 0 || slot >= p.num_slots) N = 0;
+  const int p_lo = p.n_sink, p_hi = N - p.n_recent;
+  const int first_page = p_lo / kPageTokens;
+  const int n_pp = p_hi > p_lo ? (p_hi - 1) / kPageTokens - first_page + 1 : 0;
+  int n_tiles, page0 = 0, ns = 0, nb = 0, rstart = 0;
+  if (!packed) {
+    ns = min(p.n_sink, N);
+    rstart = max(p.n_sink, N - p.n_recent);
+    nb = ns + max(0, N - rstart);
+    n_tiles = (nb + kT - 1) / kT;
+  } else {
+    page0 = itm.y;
+    n_tiles = 2 * min(itm.z, first_page + n_pp - page0);
+    if (n_tiles <= 0) return;
+  }
+
+  if (packed && p.num_pages <= 0) return;  // packed tokens without a page pool: nothing to read
+  // every role runs the same n_steps = n_tiles + 1 steps (one barrier each), rounded up to a
+  // multiple of 3 so the unpack waves cycle through their three register buffers in step
+  const int n_steps = (n_tiles + 3) / 3 * 3;
+
+  const int head0 = hg * kHW;
+  const float c_log2 = p.scale_log2e;
+  const int64_t row0 = (int64_t)item * p.heads + head0;  // first workspace row of this workgroup
+
+  if (w < 2) {
+    // ====================== QK waves: heads head0 + 32w + 16hb + L16, hb = 0, 1 ======================
+    // queries: A operand of QK 16x16x32 (lane: head .. + L16, positions 32 ks + 8 G + j)
+    f16x8 qreg[2][16];  // content K steps; the RoPE steps and the zero-term step live in LDS
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float qs[kGroups];
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) qs[g] = 0.f;
+      const uint16_t* qh = p.q + ((int64_t)b * p.heads + head0 + 32 * w + 16 * hb + L16) * kD;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(qh + 32 * ks + 8 * G);
+        const uint4 hv = ks < 16 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw);
+        const f16x8 fr = __builtin_bit_cast(f16x8, hv);
+        if (ks < 16) qreg[hb][ks] = fr;
+        else sm.qfrag[ks - 16][w][hb][lane] = fr;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += (float)fr[j];
+        qs[ks < 16 ? ks / 2 : 8] += sum;
+      }
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        qs[g] += __shfl_xor(qs[g], 16, 64);
+        qs[g] += __shfl_xor(qs[g], 32, 64);
+        qs[g] *= c_log2;
+      }
+      // zero-term step, k = 8 G + j: G0 hi(qsum_j), G1 lo(qsum_j) against z_j; G2 / G3 hi / lo of
+      // qsum_8 in slot j = 0 against z_8 (the other slots meet zero columns)
+      f16x8 z;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = G < 2 ? qs[j] : (j == 0 ? qs[8] : 0.f);
+        const f16 hi = (f16)x;
+        const f16 lo = (f16)(x - (float)hi);
+        z[j] = (G & 1) ? lo : hi;
+      }
+      sm.qfrag[2][w][hb][lane] = z;
+    }
+    float m_run[2][4], l_part[2][4];  // heads .. + 16hb + 4G + i (the lane's D rows)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m_run[hb][i] = -__builtin_inff();
+        l_part[hb][i] = 0.f;
+      }
+    __syncthreads();  // first tile unpacked, query fragments visible
+
+    for (int k = 0; k < n_steps; ++k) {
+      if (k < n_tiles) {
+        const int sl = k % kSlots, pb = k & 1;
+        const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
+        const lds_ptr<f16x8> qf = lds_opaque(&sm.qfrag[0][w][0][lane]);  // + 256 step + 64 hb
+        // lane (token L16 of each 16-token block, heads .. + 16hb + 4G + i)
+        f32x4 S[2][2];
+        {
+          const lds_ptr<float> sqp = lds_opaque(&sm.sq[sl][0][0]) + 2 * L16;
+          const lds_ptr<f16> k0 = tb + L16 * kS + 8 * G;
+          const lds_ptr<f16> k1 = k0 + 16 * kS;
+          f32x4 s[2][2];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // software pipeline: the tile operands and scales of group g + kAhead are requested
+          // before group g multiplies (the scheduling fences keep the requests in place)
+          constexpr int kAhead = 2;
+          f16x8 kf[kAhead][4];
+          f32x2 scf[kAhead];
+          auto request = [&](int g) {
+            kf[g % kAhead][0] = lds_load<f16x8>(k0 + 64 * g);
+            kf[g % kAhead][1] = lds_load<f16x8>(k1 + 64 * g);
+            kf[g % kAhead][2] = lds_load<f16x8>(k0 + 64 * g + 32);
+            kf[g % kAhead][3] = lds_load<f16x8>(k1 + 64 * g + 32);
+            scf[g % kAhead] = lds_load<f32x2>(sqp + g * kT);
+          };
+#pragma unroll
+          for (int g = 0; g < kAhead; ++g) request(g);
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) {
+            const int r = g % kAhead;
+            f32x4 c[2][2];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              const f16x8 q0 = g < 8 ? qreg[hb][2 * g] : lds_load<f16x8>(qf + 64 * hb);
+              const f16x8 q1 = g < 8 ? qreg[hb][2 * g + 1] : lds_load<f16x8>(qf + 256 + 64 * hb);
+              const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+              c[hb][0] = mfma16(q0, kf[r][0], z4);
+              c[hb][1] = mfma16(q0, kf[r][1], z4);
+              c[hb][0] = mfma16(q1, kf[r][2], c[hb][0]);
+              c[hb][1] = mfma16(q1, kf[r][3], c[hb][1]);
+            }
+            const f32x2 sc = scf[r];
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + kAhead < kGroups) request(g + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              s[hb][0] += sc[0] * c[hb][0];
+              s[hb][1] += sc[1] * c[hb][1];
+            }
+          }
+          // zero terms of all nine groups
+          const int zc = kZ + 8 * (G >> 1);
+          const f16x8 zr0 = lds_load<f16x8>(tb + L16 * kS + zc);
+          const f16x8 zr1 = lds_load<f16x8>(tb + (16 + L16) * kS + zc);
+          const f32x2 bv = lds_load<f32x2>(lds_opaque(&sm.bias[sl][0]) + 2 * L16);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const f16x8 qz = lds_load<f16x8>(qf + 512 + 64 * hb);
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            S[hb][0] = s[hb][0] + mfma16(qz, zr0, z4) + bv[0];
+            S[hb][1] = s[hb][1] + mfma16(qz, zr1, z4) + bv[1];
+          }
+        }
+        // online softmax; a head's running max is refreshed only when one of its scores
+        // exceeds it by more than kRescale
+        bool need = false;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            need |= (S[hb][0][i] > m_run[hb][i] + kRescale) | (S[hb][1][i] > m_run[hb][i] + kRescale);
+        const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+        float alpha[2][4];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) alpha[hb][i] = 1.f;
+        if (any) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float mx = row16_max(fmaxf(S[hb][0][i], S[hb][1][i]));
+              const float m_new = fmaxf(m_run[hb][i], mx);
+              alpha[hb][i] = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[hb][i] - m_new);
+              m_run[hb][i] = m_new;
+              l_part[hb][i] *= alpha[hb][i];
+            }
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          f16x4 pz[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float mu = m_run[hb][i] == -__builtin_inff() ? 0.f : m_run[hb][i];
+            const float e0 = __builtin_amdgcn_exp2f(S[hb][0][i] - mu);
+            const float e1 = __builtin_amdgcn_exp2f(S[hb][1][i] - mu);
+            l_part[hb][i] += e0 + e1;
+            pz[0][i] = (f16)e0;
+            pz[1][i] = (f16)e1;
+          }
+          const int hc = 32 * w + 16 * hb + 4 * G;  // first head column of the lane's rows
+          f16* prow = &sm.probT[pb][L16][hc];
+          *reinterpret_cast<f16x4*>(prow) = pz[0];
+          *reinterpret_cast<f16x4*>(prow + 16 * kPT) = pz[1];
+          if (L16 == 0)
+            *reinterpret_cast<f32x4*>(&sm.alpha[pb][hc]) = f32x4{alpha[hb][0], alpha[hb][1], alpha[hb][2], alpha[hb][3]};
+        }
+        if (lane == 0) sm.resc[pb][w] = any ? 1 : 0;
+      }
+      __syncthreads();
+    }
+    // running max and sum of the heads of this wave
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float l_tot = row16_sum(l_part[hb][i]);
+        if (L16 == 0) {
+          const int64_t hrow = row0 + 32 * w + 16 * hb + 4 * G + i;
+          p.ws_ml[2 * hrow] = m_run[hb][i];
+          p.ws_ml[2 * hrow + 1] = l_tot;
+        }
+      }
+  } else if (w < 4) {
+    // =========================== unpack waves: tiles into the LDS ring ===========================
+    const int ft = tid - 128;  // 0 .. 127
+    const bool meta_lane = ft < kT;  // wave 2, lanes 0 .. 31: metadata of token ft
+    const int64_t slot_row = (int64_t)slot * p.max_pages;
+    // packed bytes of tile min(t, n_tiles - 1) (half t % 2 of page page0 + t / 2) into registers;
+    // every call issues the same loads, so the compiler's load counting stays exact
+    auto load = [&](int t, TileRegs<BITS_C>& R) {
+      t = min(t, n_tiles - 1);
+      const int page_idx = page0 + (t >> 1), hs = t & 1;
+      int64_t pg = (page_idx < p.max_pages) ? (int64_t)scalar_load(p.block_table + slot_row + page_idx) : 0;
+      if (pg < 0 || pg >= p.num_pages) pg = 0;  // contract violation: wrong values, no fault
+      const uint8_t* base = p.pages + pg * (int64_t)GE::PB;
+      const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + hs * kT * GE::CB);
+      const uint32_t* srcR = reinterpret_cast<const uint32_t*>(base + GE::ROPE0 + hs * kT * kDr / 2);
+#pragma unroll
+      for (int i = 0; i < GE::CPT; ++i) R.c[i] = srcC[ft + 128 * i];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) R.r[i] = srcR[ft + 128 * i];
+      if (w == 2) {
+        const uint3* srcM = reinterpret_cast<const uint3*>(base + GE::META0 + hs * kT * 4 * kGroups) + 3 * min(ft, kT - 1);
+        if (meta_lane) {
+#pragma unroll
+          for (int i = 0; i < 3; ++i) R.m[i] = srcM[i];
+        }
+      }
+    };
+    // unpack tile t into ring slot t % 3
+    auto fill = [&](int t, const TileRegs<BITS_C>& R) {
+      const int sl = t % kSlots;
+      f16* tile = &sm.tile[sl][0];
+      if (!packed) {
+        for (int e = ft; e < kT * (kD / 8); e += 128) {
+          const int r = e / (kD / 8), m = e % (kD / 8);
+          const int j = t * kT + r;
+          uint4 o = make_uint4(0, 0, 0, 0);
+          if (j < nb) {
+            const uint16_t* src;
+            if (j < ns) {
+              src = p.sink + ((int64_t)slot * p.n_sink + j) * kD;
+            } else {
+              const int tt = rstart + (j - ns);
+              src = p.recent + ((int64_t)slot * p.n_recent + tt % p.n_recent) * kD;
+            }
+            const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * m);
+            o = m < kDc / 8 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw);
+          }
+          *reinterpret_cast<uint4*>(&tile[r * kS + 8 * m]) = o;
+        }
+        if (meta_lane) {
+          const int r = ft;
+          const bool valid = t * kT + r < nb;
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) sm.sq[sl][g][sq_pos(r)] = valid ? c_log2 : 0.f;
+#pragma unroll
+          for (int g = 0; g < 8; ++g) sm.svh[sl][g][r] = valid ? (f16)1.f : (f16)0.f;
+          sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
+          *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) = make_uint4(0, 0, 0, 0);
+        }
+        return;
+      }
+      // content codes: consecutive lanes write consecutive 16-byte (C4) or 32-byte (C2) runs
+#pragma unroll
+      for (int i = 0; i < GE::CPT; ++i) {
+        const int u = ft + 128 * i;
+        const int r = u / GE::DPR, d = u % GE::DPR;
+        f16* dst = &tile[r * kS];
+        if (BITS_C == 4) {
+          *reinterpret_cast<uint4*>(dst + 8 * d) = unpack4(R.c[i]);
+        } else {
+          uint4 x0, x1;
+          unpack2(R.c[i], x0, x1);
+          *reinterpret_cast<uint4*>(dst + 16 * d) = x0;
+          *reinterpret_cast<uint4*>(dst + 16 * d + 8) = x1;
+        }
+      }
+      // RoPE-key codes: dword u holds channels 8 (u % 8) .. +7 of token u / 8
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = ft + 128 * i;
+        *reinterpret_cast<uint4*>(&tile[(u >> 3) * kS + kDc + 8 * (u & 7)]) = unpack4(R.r[i]);
+      }
+      if (meta_lane) {  // metadata of token ft: (s | z << 16) for the nine groups
+        const int r = ft;
+        const uint32_t md[kGroups] = {R.m[0].x, R.m[0].y, R.m[0].z, R.m[1].x, R.m[1].y,
+                                      R.m[1].z, R.m[2].x, R.m[2].y, R.m[2].z};
+        const int tok = (page0 + (t >> 1)) * kPageTokens + (t & 1) * kT + r;
+        const bool valid = tok >= p_lo && tok < p_hi;
+        f16 zh[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          const float sc = valid ? bf16f(md[g] & 0xFFFFu) : 0.f;
+          zh[g] = (f16)(valid ? bf16f(md[g] >> 16) : 0.f);
+          sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
+          if (g < 8) sm.svh[sl][g][r] = (f16)sc;
+        }
+        uint4 z0;
+        z0.x = __builtin_bit_cast(uint32_t, f16x2{zh[0], zh[1]});
+        z0.y = __builtin_bit_cast(uint32_t, f16x2{zh[2], zh[3]});
+        z0.z = __builtin_bit_cast(uint32_t, f16x2{zh[4], zh[5]});
+        z0.w = __builtin_bit_cast(uint32_t, f16x2{zh[6], zh[7]});
+        *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = z0;
+        *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
+            make_uint4(__builtin_bit_cast(uint32_t, f16x2{zh[8], (f16)0.f}), 0, 0, 0);
+        sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
+      }
+    };
+    if (packed) {
+      // tile t lives in R(t % 3); step k requests tile k + 3 into the registers tile k held and
+      // unpacks tile k + 1 (the waits for its loads, two batches deep, come from the compiler)
+      TileRegs<BITS_C> R0, R1, R2;
+      auto step = [&](int k, TileRegs<BITS_C>& next, const TileRegs<BITS_C>& cur) {
+        load(k + 3, next);
+        if (k + 1 < n_tiles) fill(k + 1, cur);
+        __syncthreads();
+      };
+      load(0, R0);
+      load(1, R1);
+      load(2, R2);
+      fill(0, R0);
+      __syncthreads();  // first tile unpacked
+      for (int k = 0; k < n_steps; k += 3) {
+        step(k, R0, R1);
+        step(k + 1, R1, R2);
+        step(k + 2, R2, R0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
+    } else {
+      const TileRegs<BITS_C> none{};
+      if (n_tiles > 0) fill(0, none);
+      __syncthreads();  // first tile unpacked
+      for (int k = 0; k < n_steps; ++k) {
+        if (k + 1 < n_tiles) fill(k + 1, none);
+        __syncthreads();
+      }
+    }
+  } else {
+    // ============ PV waves: content groups 2v, 2v + 1 for all 64 heads ============
+    const int v = w - 4;
+    f32x4 oz = {0.f, 0.f, 0.f, 0.f};  // rows z index 4G + i, column head 16v + L16: sum_t p z
+    f32x16 O[2][4];                    // [head block][channel block]
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) O[hb][cb] = f32x16{};
+    __syncthreads();  // first tile unpacked
+
+    for (int k = 0; k < n_steps; ++k) {
+      if (k >= 1 && k <= n_tiles) {
+        // accumulate tile k - 1 (ring slot (k - 1) % 3, probabilities of step k - 1)
+        const int sl = (k - 1) % kSlots, pb = (k - 1) & 1;
+        const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
+        const lds_ptr<int> rf = lds_opaque(&sm.resc[pb][0]);
+        if (rf[0] | rf[1]) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const float a = sm.alpha[pb][32 * hb + l32];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) O[hb][cb] *= a;
+          }
+          oz *= sm.alpha[pb][16 * v + L16];
+        }
+        const lds_ptr<f16> ptb = lds_opaque(&sm.probT[pb][0][0]);
+        // request every operand of the step before multiplying (the fence keeps them together)
+        // zero-term sums for heads 16v + L16 (A: z rows from the zero-term columns, k: tokens
+        // 4G + j | 16 + 4G + j; B: the same tokens' probabilities)
+        const lds_ptr<f16> za = tb + (4 * G + (L16 >> 2)) * kS + kZ + 4 * (L16 & 3);
+        const lds_ptr<f16> pa = ptb + (4 * G + (L16 >> 2)) * kPT + 16 * v + 4 * (L16 & 3);
+        const f16x8 zA = cat(lds_tr4(za), lds_tr4(za + 16 * kS));
+        const f16x8 zP = cat(lds_tr4(pa), lds_tr4(pa + 16 * kPT));
+        const lds_ptr<f16> svw = lds_opaque(&sm.svh[sl][2 * v][0]);
+        f16x8 A[2][4], P[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int t0 = 16 * ks + 4 * half;  // k slots: tokens t0 + j (j < 4), t0 + 8 + (j - 4)
+          const int rsel = t0 + ((lane & 15) >> 2), csel = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          const lds_ptr<f16> va = tb + rsel * kS + 128 * v + csel;
+          const lds_ptr<f16> pbp = ptb + rsel * kPT + csel;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) A[ks][cb] = cat(lds_tr4(va + 32 * cb), lds_tr4(va + 8 * kS + 32 * cb));
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) P[ks][hb] = cat(lds_tr4(pbp + 32 * hb), lds_tr4(pbp + 8 * kPT + 32 * hb));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        oz = mfma16(zA, zP, oz);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            const int t0 = 16 * ks + 4 * half;
+            const f16x8 sv = cat(lds_load<f16x4>(svw + gi * kT + t0), lds_load<f16x4>(svw + gi * kT + t0 + 8));
+            const f16x8 b0 = P[ks][0] * sv, b1 = P[ks][1] * sv;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const int cb = 2 * gi + c;
+              O[0][cb] = mfma32(A[ks][cb], b0, O[0][cb]);
+              O[1][cb] = mfma32(A[ks][cb], b1, O[1][cb]);
+            }
+          }
+      }
+      __syncthreads();
+    }
+    // unnormalised partial output and zero-term sums
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float* dh = p.ws_o + (row0 + 32 * hb + l32) * kDc;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int pos = 128 * v + 32 * cb + 8 * (i >> 2) + 4 * half + (i & 3);
+          dh[8 * (pos >> 3) + perm8<BITS_C>(pos & 7)] = O[hb][cb][i];
+        }
+    }
+    if (G < 2) {
+      const int64_t hrow = row0 + 16 * v + L16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.ws_z[hrow * 8 + 4 * G + i] = oz[i];
+    }
+  }
+}
+
+template <int BITS_C>
+hipError_t launch64(const DecodeParams& p, hipStream_t stream) {
+  const size_t smem = sizeof(Smem64<BITS_C>);
+  auto kern = decode64_kernel<BITS_C>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), smem, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode64(const DecodeParams& p, int bits_c, hipStream_t stream) {
+  if (bits_c == 4) return launch64<4>(p, stream);
+  if (bits_c == 2) return launch64<2>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla
