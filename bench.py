@@ -125,7 +125,7 @@ def cpu_baseline(w, budget_s):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("decode.hip", "decode64.hip", "decode_common.h", "mla_internal.h"):
+    for f in ("decode.hip", "decode64.hip", "decode16.hip", "decode_common.h", "mla_internal.h"):
         h.update(open(os.path.join(ROOT, "bit_mla_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

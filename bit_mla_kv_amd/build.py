@@ -26,6 +26,7 @@ UNITS = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
     "decode64.hip": [],
+    "decode16.hip": [],
     "plan.hip": [],
     "abi.hip": [],
 }

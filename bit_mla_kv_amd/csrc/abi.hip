@@ -147,7 +147,7 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
     return fail(MLA_LOWBIT_ERR_INVALID_ARG, "batch=%d max_seq_len=%d must be >= 0", batch, max_seq_len);
   mla::DecodeConfig cfg;
   if (!mla::decode_config(num_heads, cache->layout.n_sink, cache->layout.n_recent, batch, max_seq_len, &cfg))
-    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "num_heads=%d unsupported (16, 32, 64 or a multiple of 128)",
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "num_heads=%d unsupported (a positive multiple of 16)",
                 num_heads);
   if (!std::isfinite(softmax_scale)) return fail(MLA_LOWBIT_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (batch == 0) return MLA_LOWBIT_OK;
@@ -190,7 +190,7 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.seq_info = reinterpret_cast<int32_t*>(wsb + wl.seq_off);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
   p.ws_z = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.z_off);
-  p.has_z = cfg.heads_per_wg == 64;  // the 64-head kernel leaves the zero-term sums to the combine
+  p.has_z = 1;  // the decode kernels leave the zero-term sums to the combine
   p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;

@@ -69,6 +69,7 @@ struct DecodeParams {
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_decode64(const DecodeParams& p, int bits_c, hipStream_t stream);
+hipError_t launch_decode16(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 

@@ -47,7 +47,7 @@
  * Supported layout: d_c = 512, d_r = 64, group = 64, page_tokens = 64,
  * bits_c in {4, 2}, bits_r = 4, 0 <= n_sink <= 64, 1 <= n_recent <= 8192
  * (n_recent >= every sequence length gives an all-bf16 cache).  num_heads
- * must be 16, 32, 64 or a multiple of 128.  Anything else returns
+ * must be a positive multiple of 16.  Anything else returns
  * MLA_LOWBIT_ERR_UNSUPPORTED.
  */
 #ifndef MLA_LOWBIT_H_

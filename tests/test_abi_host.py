@@ -84,7 +84,10 @@ def test_decode_validation(m):
 
     assert call(cache=None) == m.ERR_INVALID_ARG
     assert call(heads=24) == m.ERR_UNSUPPORTED
-    assert call(heads=96) == m.ERR_UNSUPPORTED
+    assert call(heads=8) == m.ERR_UNSUPPORTED
+    assert call(heads=0) == m.ERR_UNSUPPORTED
+    # 96 heads (six 16-head groups) are supported: the check gets as far as the workspace size
+    assert call(heads=96) == m.ERR_WORKSPACE
     assert call(wsb=ws - 1) == m.ERR_WORKSPACE
     assert "workspace" in L.mla_lowbit_last_error().decode()
     assert call(ws=0x100010) == m.ERR_INVALID_ARG          # misaligned workspace
@@ -100,11 +103,12 @@ def test_decode_validation(m):
 
 def test_workspace_monotone(m):
     lay = m.make_layout(4)
-    for h in (16, 32, 64, 128, 256):
+    for h in (16, 32, 48, 64, 96, 128, 256):
         a = m.decode_workspace_bytes(lay, 4, h, 1024)
         b = m.decode_workspace_bytes(lay, 4, h, 131072)
         assert 0 < a <= b
-    assert m.decode_workspace_bytes(lay, 4, 48, 1024) == 0
+    for h in (0, 8, 40):
+        assert m.decode_workspace_bytes(lay, 4, h, 1024) == 0
 
 
 def test_status_strings(m):

@@ -1,0 +1,71 @@
+"""Full-size parity (marked gpu): every workload the benchmark times, at its full size and in the
+launch configuration it times (one quantize-append of a token per sequence, then the decode with the
+default split plan), checked on sampled (sequence, head) outputs that the oracle computes one by one.
+
+Sampled sequences: the first, the last and one drawn from the workload's seed; sampled heads: the
+first, the last and one drawn per sequence.  Each sampled output row is held to the same bound as the
+small-size tests (E <= 2e-3 after the bf16 store, |lse error| <= 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import oracle
+from parity import E_TOL, LSE_TOL, bf16_tensor_to_f64, e_metric
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_mla_kv_amd as m
+from bit_mla_kv_amd import cache_builder as cb
+
+FULL = ["dsv2lite_c4r4_32k", "dsv2lite_c4r4_128k", "dsv3_c4r4_128k", "dsv3_c2r4_128k", "mixed_c4r4_serving"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = mi.workload(name)
+    B, H = w.batch, w.heads
+    dev = torch.device("cuda:0")
+    final = w.seq_lens.astype(np.int64)
+    start = final - 1
+    layout = m.make_layout(w.bits_c)
+    perm = mi.page_permutation(w.seed, int(((final + 63) // 64).sum()) + 8)
+    cache = cb.allocate_for(layout, start, perm, spare_tokens=1, device=dev)
+    outl = mi.outlier_channels(w.seed)
+    pick = np.random.default_rng(1000 + w.seed)
+    seqs = sorted({0, B - 1, int(pick.integers(B))})
+    new = np.empty((B, 576), np.uint16)
+    kept = {}
+    for b in range(B):
+        rows = mi.rows(w.seed, b, int(final[b]), outl, threads=16)
+        cb.prefill(cache, b, rows[:start[b]])
+        new[b] = rows[start[b]]
+        if b in seqs:
+            kept[b] = rows
+        del rows
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    m.quantize_append(cache, cb.to_device_bf16(new, dev), slots,
+                      torch.tensor(start, dtype=torch.int32, device=dev),
+                      torch.tensor(final, dtype=torch.int32, device=dev))
+    q_host = mi.queries(w.seed, B, H)
+    q = cb.to_device_bf16(q_host.reshape(B * H, -1), dev).view(B, H, 576)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(layout, B, H, int(final.max()), dev)
+    m.decode(cache, q, slots, torch.tensor(final, dtype=torch.int32, device=dev), int(final.max()), w.scale,
+             out, lse, ws)
+    torch.cuda.synchronize()
+    o_all = bf16_tensor_to_f64(out)
+    l_all = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all)), name
+    for b in seqs:
+        heads = sorted({0, H - 1, int(pick.integers(H))})
+        ro, rl = oracle.decode_sequence(kept[b], q_host[b], w.scale, w.bits_c, heads=heads)
+        E = e_metric(o_all[b, heads], ro)
+        assert E.max() <= E_TOL, f"{name} seq {b} heads {heads}: E {E}"
+        err = np.abs(l_all[b, heads] - rl)
+        assert err.max() <= LSE_TOL, f"{name} seq {b} heads {heads}: lse err {err}"

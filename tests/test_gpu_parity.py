@@ -148,7 +148,7 @@ def test_decode_tiny_c4r4():
 EDGE_LENS = [0, 1, 3, 4, 5, 63, 64, 65, 131, 132, 133, 134, 196, 197, 198, 260, 700, 2049]
 
 
-@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("heads", [16, 32, 48, 64, 96, 128])
 @pytest.mark.parametrize("bits_c", [4, 2])
 def test_decode_edge_lengths(heads, bits_c):
     seed = 30 + heads + bits_c
