@@ -386,33 +386,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       // (vector types: a struct load can be split into loads that lose their object)
       const u32x2 rw = lds_load<u32x2>(sb + (zo + o_r));
-      f32x4 cg[kGroups];
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        // block t + 1, group g: K operands (C4: units 2g, 2g + 1 of the token's row, the lane's 8
-        // bytes at 8 G; C2: unit g, the lane's dword at 4 G)
-        f16x8 k0, k1;
-        if (g == 8) {
-          k0 = __builtin_bit_cast(f16x8, unpack4(rw.x));
-          k1 = __builtin_bit_cast(f16x8, unpack4(rw.y));
-        } else if (BITS_C == 4) {
-          const u32x2 v = lds_load<u32x2>(sb + (zo + o_c + 32 * g));
-          k0 = __builtin_bit_cast(f16x8, unpack4(v.x));
-          k1 = __builtin_bit_cast(f16x8, unpack4(v.y));
-        } else {
-          uint4 x0, x1;
-          unpack2(lds_load<uint32_t>(sb + (zo + o_c + 16 * g)), x0, x1);
-          k0 = __builtin_bit_cast(f16x8, x0);
-          k1 = __builtin_bit_cast(f16x8, x1);
-        }
-        // block t, group g: V^T operands of channel positions 64 g .. 64 g + 63
-        f16x4 va[4];
+      // Per group: the LDS reads of group g + 1 are issued, then group g's codes are unpacked and
+      // multiplied (the fences keep this order, so only two groups' operands are live), and each
+      // group's partial is scaled into s one group later.
+      // K operand words of block t + 1 (C4: units 2g, 2g + 1 of the token's row, the lane's 8 bytes
+      // at 8 G; C2: unit g, the lane's dword at 4 G; group 8: the RoPE codes)
+      auto rd_k = [&](int g) -> u32x2 {
+        if (g == 8) return rw;
+        if (BITS_C == 4) return lds_load<u32x2>(sb + (zo + o_c + 32 * g));
+        return u32x2{lds_load<uint32_t>(sb + (zo + o_c + 16 * g)), 0u};
+      };
+      // V^T operands of block t, channel positions 64 g .. 64 g + 63
+      auto rd_v = [&](int g, f16x4 (&va)[4]) {
         if (g < 8 && do_pv) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) va[c] = lds_tr4((lds_ptr<f16>)(tb + (o_vtr + 32 * (4 * g + c))));
         }
-        cg[g] = mfma32k(qreg[2 * g], k0, f32x4{0.f, 0.f, 0.f, 0.f});
-        cg[g] = mfma32k(qreg[2 * g + 1], k1, cg[g]);
+      };
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, cprev;
+      u32x2 kw_next = rd_k(0);
+      f16x4 va_next[4];
+      rd_v(0, va_next);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        const u32x2 kw = kw_next;
+        f16x4 va[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) va[c] = va_next[c];
+        if (g + 1 < kGroups) {
+          kw_next = rd_k(g + 1);
+          rd_v(g + 1, va_next);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 k0, k1;
+        if (g == 8 || BITS_C == 4) {
+          k0 = __builtin_bit_cast(f16x8, unpack4(kw.x));
+          k1 = __builtin_bit_cast(f16x8, unpack4(kw.y));
+        } else {
+          uint4 x0, x1;
+          unpack2(kw.x, x0, x1);
+          k0 = __builtin_bit_cast(f16x8, x0);
+          k1 = __builtin_bit_cast(f16x8, x1);
+        }
+        f32x4 cg = mfma32k(qreg[2 * g], k0, f32x4{0.f, 0.f, 0.f, 0.f});
+        cg = mfma32k(qreg[2 * g + 1], k1, cg);
         if (g < 8) {
           *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + 128 * g)) = k0;
           *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + 128 * g + 16)) = k1;
@@ -422,27 +439,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             for (int c = 0; c < 4; ++c) O[4 * g + c] = mfma16k(va[c], bop, O[4 * g + c]);
           }
         }
+        if (g > 0) s += bf16f(mw[g - 1] & 0xFFFFu) * cprev;
+        cprev = cg;
+        __builtin_amdgcn_sched_barrier(0);
       }
+      s += bf16f(mw[kGroups - 1] & 0xFFFFu) * cprev;
       if (do_pv) oz = mfma16k(za, pb, oz);
-      f16x8 zf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) zf[j] = (f16)(G < 2 ? bf16f(mw[j] >> 16) : (j == 0 ? bf16f(mw[8] >> 16) : 0.f));
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) s += bf16f(mw[g] & 0xFFFFu) * cg[g];
-      s = mfma32k(qz, zf, s * c_log2) + (valid ? 0.f : -__builtin_inff());
-      if (G == 0) {
-        f16x8 z8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) z8[j] = (f16)bf16f(mw[j] >> 16);
-        *reinterpret_cast<lds_ptr<f16x8>>(tb + o_zwr) = z8;
-        *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + 16)) = f16x8{};
-#pragma unroll
-        for (int g = 0; g < 8; ++g) *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 32 * g)) = (f16)bf16f(mw[g] & 0xFFFFu);
+      // block t + 1's Z and SV tile entries: lane (token L16, G) writes groups 2G, 2G + 1 (lanes G = 0
+      // also z_8 into column 8; columns 9 .. 15 stay zero), then reads its zero-term operand back:
+      // z_0 .. z_7 (G < 2) or z_8 and seven zeros (G >= 2)
+      {
+        const u32x2 mp = lds_load<u32x2>(sb + (zo + o_m + 8 * G));
+        const uint32_t m0 = valid ? mp.x : 0u, m1 = valid ? mp.y : 0u;
+        *reinterpret_cast<lds_ptr<f16x2>>(tb + (o_zwr + 4 * G)) = f16x2{(f16)bf16f(m0 >> 16), (f16)bf16f(m1 >> 16)};
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G)) = (f16)bf16f(m0 & 0xFFFFu);
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G + 32)) = (f16)bf16f(m1 & 0xFFFFu);
+        if (G == 0) *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + 16)) = (f16)bf16f(mw[8] >> 16);
       }
+      const f16x8 zf = lds_load<f16x8>(tb + (o_zwr + 16 * (G >> 1)));
+      s = mfma32k(qz, zf, s * c_log2) + (valid ? 0.f : -__builtin_inff());
       return s;
     };
 
+    if (G == 0) *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + 16)) = f16x8{};  // Z columns 8 .. 15
     // while block t's PV and block t + 1's QK run, blocks t + 2, t + 3 are in flight
     stage(0, page_id(0));
     stage(1, page_id(1));
