@@ -53,6 +53,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int pos = p.token_pos[tok];
   if (slot < 0 || slot >= p.num_slots || pos < 0) return;
   const uint16_t* row = p.kv + (int64_t)tok * kD;
+  // every load of the token's row is requested before any is used: the lane's channel of each
+  // group, and the row's 16-byte chunks lane, 64 + lane for the bf16 copies
+  float xs[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) xs[g] = bf16_to_float(row[g * kGroup + lane]);
+  const uint4* src = reinterpret_cast<const uint4*>(row);
+  const uint4 chunk0 = src[lane];
+  const uint4 chunk1 = lane < kD / 8 - 64 ? src[64 + lane] : make_uint4(0, 0, 0, 0);
 
   // page row of this token (skip packed write if the table entry is out of range)
   uint8_t* prow_c = nullptr;
@@ -76,7 +84,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     for (int g = 0; g < kGroups; ++g) {
       const int bits = g < 8 ? p.bits_c : 4;
       const int lb = (1 << bits) - 1;
-      const float x = bf16_to_float(row[g * kGroup + lane]);
+      const float x = xs[g];
       const float mn = wave_min(x);
       const float mx = wave_max(x);
       const float range = mx - mn;
@@ -107,14 +115,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 
   // bf16 copies: 1152 bytes = 72 x 16 bytes per row
-  const uint4* src = reinterpret_cast<const uint4*>(row);
   if (pos < p.n_sink) {
     uint4* dst = reinterpret_cast<uint4*>(p.sink + ((int64_t)slot * p.n_sink + pos) * kD);
-    for (int i = lane; i < kD / 8; i += 64) dst[i] = src[i];
+    dst[lane] = chunk0;
+    if (lane < kD / 8 - 64) dst[64 + lane] = chunk1;
   }
   if (pos >= p.slot_len_after[slot] - p.n_recent) {
     uint4* dst = reinterpret_cast<uint4*>(p.recent + ((int64_t)slot * p.n_recent + pos % p.n_recent) * kD);
-    for (int i = lane; i < kD / 8; i += 64) dst[i] = src[i];
+    dst[lane] = chunk0;
+    if (lane < kD / 8 - 64) dst[64 + lane] = chunk1;
   }
 }
 

@@ -17,7 +17,7 @@ namespace mla {
 namespace {
 using namespace dev;
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 64;  // one wave: scans are lane shuffles, no workgroup barriers
 
 __device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, int* first_page) {
   int N = p.seq_len[b];
@@ -28,26 +28,20 @@ __device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, in
   return p_hi > p_lo ? (p_hi - 1) / kPageTokens - *first_page + 1 : 0;
 }
 
-// block-wide exclusive scan of one int per thread; returns the block total in *total
-__device__ int block_exclusive_scan(int v, int* sh, int* total) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int add = t >= off ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += add;
-    __syncthreads();
+// exclusive scan over the 64 lanes of the wave; *total gets the sum
+__device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
+  const int lane = threadIdx.x;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
   }
-  const int incl = sh[t];
-  *total = sh[kPlanThreads - 1];
-  __syncthreads();
-  return incl - v;
+  *total = __shfl(x, 63, 64);
+  return x - v;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
-  __shared__ int sh[kPlanThreads];
-  __shared__ long long tot_sh;
   const int t = threadIdx.x;
   // total packed pages
   long long local = 0;
@@ -55,16 +49,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     int fp;
     local += seq_packed_pages(p, b, &fp);
   }
-  if (t == 0) tot_sh = 0;
-  __syncthreads();
-  atomicAdd(reinterpret_cast<unsigned long long*>(&tot_sh), (unsigned long long)local);
-  __syncthreads();
-  const long long total = tot_sh;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
+  const long long total = local;
   int pps = (int)std::min<long long>((total + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
   if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
 
-  // pass 1: counts of full / tail items, scanned in chunks of kPlanThreads sequences
+  // pass 1: counts of full / tail items, scanned in chunks of 64 sequences (lane t owns sequence
+  // b0 + t in both passes, so it reads back only what it wrote itself)
   int full_base = 0, tail_base = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kPlanThreads) {
     const int b = b0 + t;
@@ -75,10 +68,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
       nt = (n % pps) != 0;
     }
     int tf, tt;
-    const int of = block_exclusive_scan(nf, sh, &tf);
-    const int ot = block_exclusive_scan(nt, sh, &tt);
+    const int of = wave_exclusive_scan(nf, &tf);
+    const int ot = wave_exclusive_scan(nt, &tt);
     if (b < p.batch) {
-      p.seq_info[4 * b + 0] = full_base + of;  // first full item (relative, fixed below)
+      p.seq_info[4 * b + 0] = full_base + of;  // first full item
       p.seq_info[4 * b + 1] = nf;
       p.seq_info[4 * b + 2] = nt ? tail_base + ot : -1;
       p.seq_info[4 * b + 3] = fp;              // first packed page (temporarily)
@@ -86,7 +79,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     full_base += tf;
     tail_base += tt;
   }
-  __syncthreads();
   const int F = full_base, T = tail_base;
   // pass 2: emit items (b, first page, pages, kind)
   for (int b = t; b < p.batch; b += kPlanThreads) {
@@ -117,8 +109,11 @@ __device__ __forceinline__ uint16_t f2bf_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// one workgroup per (sequence, head): 128 threads x 4 channels
+// one workgroup per (sequence, head): 128 threads x 4 channels.  A sequence's partial rows are
+// merged eight at a time: the loads of a batch are all requested before any is used, and the
+// batch joins a running max-shifted sum.
 __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
+  constexpr int kBatch = 8;
   const int b = blockIdx.x / p.heads;
   const int h = blockIdx.x % p.heads;
   const int t = threadIdx.x;
@@ -126,27 +121,41 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
   const int tl = p.seq_info[4 * b + 2], bi = p.seq_info[4 * b + 3];
   const int n_rows = nf + (tl >= 0) + (bi >= 0);
   auto item_of = [&](int k) { return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi); };
+  const int g = t / 16;  // channels 4t..4t+3 lie in group t/16
 
-  float M = -__builtin_inff();
-  for (int k = 0; k < n_rows; ++k) {
-    const int64_t row = (int64_t)item_of(k) * p.heads + h;
-    if (p.ws_ml[2 * row + 1] > 0.f) M = fmaxf(M, p.ws_ml[2 * row]);
-  }
+  float M = -__builtin_inff(), den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n_rows; k0 += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    f32x4 ov[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int k = min(k0 + j, n_rows - 1);  // past the end: re-read the last row, weight 0
+      const int64_t row = (int64_t)item_of(k) * p.heads + h;
+      mv[j] = p.ws_ml[2 * row];
+      lv[j] = k0 + j < n_rows ? p.ws_ml[2 * row + 1] : 0.f;
+      ov[j] = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
+      if (p.has_z) ov[j] += p.ws_z[row * 8 + g];
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (lv[j] > 0.f) mb = fmaxf(mb, mv[j]);
+    if (mb == -__builtin_inff()) continue;  // nothing valid yet
+    const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+    acc *= r;
+    den *= r;
+    M = mb;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (!(lv[j] > 0.f)) continue;
+      const float wgt = __builtin_amdgcn_exp2f(mv[j] - M);
+      den += wgt * lv[j];
+      acc += wgt * ov[j];
+    }
+  }
   float L = -__builtin_inff();
   if (M != -__builtin_inff()) {
-    float den = 0.f;
-    const int g = t / 16;  // channels 4t..4t+3 lie in group t/16
-    for (int k = 0; k < n_rows; ++k) {
-      const int64_t row = (int64_t)item_of(k) * p.heads + h;
-      const float l = p.ws_ml[2 * row + 1];
-      if (!(l > 0.f)) continue;
-      const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * row] - M);
-      den += wgt * l;
-      f32x4 v = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
-      if (p.has_z) v += p.ws_z[row * 8 + g];
-      acc += wgt * v;
-    }
     acc *= 1.f / den;
     L = M + __log2f(den);
   }

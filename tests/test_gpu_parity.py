@@ -162,6 +162,20 @@ def test_decode_edge_lengths(heads, bits_c):
     assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0].cpu().numpy()))  # N = 0
 
 
+@pytest.mark.parametrize("heads", [16, 64])
+def test_decode_many_sequences(heads):
+    """130 sequences (the split plan scans sequences 64 at a time), lengths 0 .. 1500 mixed."""
+    rng = np.random.default_rng(47 + heads)
+    lens = [int(x) for x in rng.integers(0, 1500, size=130)]
+    lens[0], lens[63], lens[64], lens[129] = 0, 133, 1, 1500
+    rows = [mi.rows(47, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(47, len(lens), heads)
+    cache = build(rows, 4, seed=47)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = reference(rows, q, 4, SCALE)
+    check(out, lse, ro, rl, f"B130 H{heads}")
+
+
 def test_decode_heads_256():
     lens = [900, 3000]
     rows = [mi.rows(41, b, n) for b, n in enumerate(lens)]
