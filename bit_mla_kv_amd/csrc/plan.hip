@@ -109,33 +109,44 @@ __device__ __forceinline__ uint16_t f2bf_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// one workgroup per (sequence, head): 128 threads x 4 channels.  A sequence's partial rows are
-// merged eight at a time: the loads of a batch are all requested before any is used, and the
-// batch joins a running max-shifted sum.
-__global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
+// One workgroup of 4 waves per (sequence, head).  Wave w merges the sequence's partial rows
+// w, w + 4, ... over all 512 channels (8 per lane), eight rows at a time with every load
+// requested before use, as a running max-shifted sum; the four waves' sums are then joined
+// through LDS.
+constexpr int kCombineWaves = 4;
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParams p) {
   constexpr int kBatch = 8;
+  __shared__ float sh_m[kCombineWaves], sh_d[kCombineWaves];
+  __shared__ f32x4 sh_acc[kCombineWaves - 1][2][64];
   const int b = blockIdx.x / p.heads;
   const int h = blockIdx.x % p.heads;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
   const int tl = p.seq_info[4 * b + 2], bi = p.seq_info[4 * b + 3];
   const int n_rows = nf + (tl >= 0) + (bi >= 0);
   auto item_of = [&](int k) { return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi); };
-  const int g = t / 16;  // channels 4t..4t+3 lie in group t/16
+  // lane's channels: 4 lane .. 4 lane + 3 (group lane / 16) and 256 + 4 lane .. (group 4 + lane / 16)
+  const int g0 = lane / 16, g1 = 4 + lane / 16;
 
   float M = -__builtin_inff(), den = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < n_rows; k0 += kBatch) {
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int my_rows = n_rows > w ? (n_rows - w + kCombineWaves - 1) / kCombineWaves : 0;
+  for (int j0 = 0; j0 < my_rows; j0 += kBatch) {
     float mv[kBatch], lv[kBatch];
-    f32x4 ov[kBatch];
+    f32x4 ov0[kBatch], ov1[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int k = min(k0 + j, n_rows - 1);  // past the end: re-read the last row, weight 0
+      const int k = w + kCombineWaves * min(j0 + j, my_rows - 1);  // past the end: last row, weight 0
       const int64_t row = (int64_t)item_of(k) * p.heads + h;
       mv[j] = p.ws_ml[2 * row];
-      lv[j] = k0 + j < n_rows ? p.ws_ml[2 * row + 1] : 0.f;
-      ov[j] = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * t);
-      if (p.has_z) ov[j] += p.ws_z[row * 8 + g];
+      lv[j] = j0 + j < my_rows ? p.ws_ml[2 * row + 1] : 0.f;
+      ov0[j] = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 4 * lane);
+      ov1[j] = *reinterpret_cast<const f32x4*>(p.ws_o + row * kDc + 256 + 4 * lane);
+      if (p.has_z) {
+        ov0[j] += p.ws_z[row * 8 + g0];
+        ov1[j] += p.ws_z[row * 8 + g1];
+      }
     }
     float mb = M;
 #pragma unroll
@@ -143,7 +154,8 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
       if (lv[j] > 0.f) mb = fmaxf(mb, mv[j]);
     if (mb == -__builtin_inff()) continue;  // nothing valid yet
     const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - mb);
-    acc *= r;
+    acc0 *= r;
+    acc1 *= r;
     den *= r;
     M = mb;
 #pragma unroll
@@ -151,20 +163,50 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
       if (!(lv[j] > 0.f)) continue;
       const float wgt = __builtin_amdgcn_exp2f(mv[j] - M);
       den += wgt * lv[j];
-      acc += wgt * ov[j];
+      acc0 += wgt * ov0[j];
+      acc1 += wgt * ov1[j];
     }
   }
-  float L = -__builtin_inff();
-  if (M != -__builtin_inff()) {
-    acc *= 1.f / den;
-    L = M + __log2f(den);
+  // join the four waves' sums in wave 0
+  if (lane == 0) {
+    sh_m[w] = M;
+    sh_d[w] = den;
   }
-  uint16_t* o = p.out + ((int64_t)b * p.heads + h) * kDc + 4 * t;
-  uint2 packed;
-  packed.x = (uint32_t)f2bf_rne(acc[0]) | ((uint32_t)f2bf_rne(acc[1]) << 16);
-  packed.y = (uint32_t)f2bf_rne(acc[2]) | ((uint32_t)f2bf_rne(acc[3]) << 16);
-  *reinterpret_cast<uint2*>(o) = packed;
-  if (p.lse && t == 0) p.lse[(int64_t)b * p.heads + h] = L * 0.69314718055994531f;
+  if (w > 0) {
+    sh_acc[w - 1][0][lane] = acc0;
+    sh_acc[w - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float Mt = M;
+#pragma unroll
+  for (int v = 1; v < kCombineWaves; ++v) Mt = fmaxf(Mt, sh_m[v]);
+  float L = -__builtin_inff();
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  if (Mt != -__builtin_inff()) {
+    float dt = 0.f;
+#pragma unroll
+    for (int v = 0; v < kCombineWaves; ++v) {
+      const float mv = v == 0 ? M : sh_m[v];
+      if (mv == -__builtin_inff()) continue;
+      const float f = __builtin_amdgcn_exp2f(mv - Mt);
+      dt += f * (v == 0 ? den : sh_d[v]);
+      o0 += f * (v == 0 ? acc0 : sh_acc[v - 1][0][lane]);
+      o1 += f * (v == 0 ? acc1 : sh_acc[v - 1][1][lane]);
+    }
+    o0 *= 1.f / dt;
+    o1 *= 1.f / dt;
+    L = Mt + __log2f(dt);
+  }
+  uint16_t* o = p.out + ((int64_t)b * p.heads + h) * kDc;
+  uint2 q0, q1;
+  q0.x = (uint32_t)f2bf_rne(o0[0]) | ((uint32_t)f2bf_rne(o0[1]) << 16);
+  q0.y = (uint32_t)f2bf_rne(o0[2]) | ((uint32_t)f2bf_rne(o0[3]) << 16);
+  q1.x = (uint32_t)f2bf_rne(o1[0]) | ((uint32_t)f2bf_rne(o1[1]) << 16);
+  q1.y = (uint32_t)f2bf_rne(o1[2]) | ((uint32_t)f2bf_rne(o1[3]) << 16);
+  *reinterpret_cast<uint2*>(o + 4 * lane) = q0;
+  *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = q1;
+  if (p.lse && lane == 0) p.lse[(int64_t)b * p.heads + h] = L * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -177,7 +219,7 @@ hipError_t launch_plan(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.batch * p.heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(64 * kCombineWaves), 0, stream, p);
   return hipGetLastError();
 }
 
