@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
     // queries: A operand (lane: head head0 + L16; K step (g, h): channels 64g + 16G + 8h .. +7)
     f16x8 qreg[18];
     f16x8 qz;
-    {
+    auto load_queries = [&]() {
       float qs[kGroups];
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) qs[g] = 0.f;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         const f16 lo = (f16)(x - (float)hi);
         qz[j] = (G & 1) ? lo : hi;
       }
-    }
+    };
     if (G == 0) *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + 16)) = f16x8{};  // Z columns 8 .. 15
 
     float m_run[4], l_part[4];  // heads 4G + i (the lane's S rows)
@@ -379,6 +379,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       stage(1, page_id(1));
       stage(2, page_id(2));
       int pg_next = page_id(3);
+      load_queries();  // its latency overlaps the first blocks' staging
       int t = 0;
       f32x4 S;
       while (true) {
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no staging left in flight
     } else {
       // bf16 tokens in virtual pages of 64, the pair's rows 16 pr .. 16 pr + 15 of each
+      load_queries();
       for (int t = 0; t < n_blocks; ++t) {
         const int j = t * kPageTokens + row;
         const bool valid = j < nb;
@@ -491,15 +493,18 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mg.z[pr][L16][4 * G + i] = oz[i];
     }
-    // pairs 2, 3 hand their outputs to pairs 0, 1; then pair 1 hands the sum to pair 0
+    // pairs 2, 3 hand their outputs to pairs 0, 1; then pair 1 hands the sum to pair 0.  Every
+    // PV wave holds the same (head, channel) in the same lane and register, so the hand-over area
+    // is laid out as the registers are: [register][lane], 16 bytes a lane, no bank conflicts.
     auto put = [&](int k) {
+      const lds_ptr<f32x4> o4 = (lds_ptr<f32x4>)&mg.o[k][0][0];
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-        *reinterpret_cast<f32x4*>(&mg.o[k][L16][16 * cb + 4 * G]) = O[cb];
+      for (int cb = 0; cb < 32; ++cb) o4[64 * cb + lane] = O[cb];
     };
     auto add = [&](int k) {
+      const lds_ptr<f32x4> o4 = (lds_ptr<f32x4>)&mg.o[k][0][0];
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) O[cb] += *reinterpret_cast<const f32x4*>(&mg.o[k][L16][16 * cb + 4 * G]);
+      for (int cb = 0; cb < 32; ++cb) O[cb] += o4[64 * cb + lane];
     };
     if (pr >= 2) put(pr - 2);
     __syncthreads();
@@ -511,13 +516,25 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       add(0);
       const int64_t orow = (int64_t)item * p.heads + head0 + L16;
       float* dst = p.ws_o + orow * kDc;
+      // Lanes G and G ^ 1 (lane ^ 16) hold the 8 channels 16 cb + 8 (G >> 1) + 0..7 between them,
+      // in the unpacking order; each takes two values from the other so that lane G even holds
+      // channels 0..3 and lane G odd channels 4..7, written as one 16-byte store.
+      const bool odd = G & 1;
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = 16 * cb + 4 * G + i;
-          dst[8 * (pos >> 3) + perm8<BITS_C>(pos & 7)] = O[cb][i];
+      for (int cb = 0; cb < 32; ++cb) {
+        const f32x4 v = O[cb];
+        f32x4 r;
+        if (BITS_C == 4) {  // even lane: channels 0 2 4 6, odd lane: 1 3 5 7
+          const float rx = __shfl_xor(odd ? v[0] : v[2], 16, 64);
+          const float ry = __shfl_xor(odd ? v[1] : v[3], 16, 64);
+          r = odd ? f32x4{rx, v[2], ry, v[3]} : f32x4{v[0], rx, v[1], ry};
+        } else {            // even lane: channels 0 4 1 5, odd lane: 2 6 3 7
+          const float rx = __shfl_xor(odd ? v[0] : v[1], 16, 64);
+          const float ry = __shfl_xor(odd ? v[2] : v[3], 16, 64);
+          r = odd ? f32x4{rx, ry, v[1], v[3]} : f32x4{v[0], v[2], rx, ry};
         }
+        *reinterpret_cast<f32x4*>(dst + 16 * cb + 8 * (G >> 1) + 4 * (G & 1)) = r;
+      }
       if (G == 0) {
         float L = 0.f, zs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -545,16 +545,30 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       }
       __syncthreads();
     }
-    // unnormalised partial output and zero-term sums
+    // unnormalised partial output and zero-term sums.  Registers 4a .. 4a + 3 of lanes l and l ^ 32
+    // hold the 8 channels 8 (16 v + 4 cb + a) + 0..7 between them, in the unpacking order; each
+    // lane takes two values from the other, so that the lower half holds channels 0..3 and the
+    // upper half channels 4..7, written as one 16-byte store.
+    const bool odd = half;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float* dh = p.ws_o + (row0 + 32 * hb + l32) * kDc;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int pos = 128 * v + 32 * cb + 8 * (i >> 2) + 4 * half + (i & 3);
-          dh[8 * (pos >> 3) + perm8<BITS_C>(pos & 7)] = O[hb][cb][i];
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 x = {O[hb][cb][4 * a], O[hb][cb][4 * a + 1], O[hb][cb][4 * a + 2], O[hb][cb][4 * a + 3]};
+          f32x4 r;
+          if (BITS_C == 4) {  // lower lane: channels 0 2 4 6, upper lane: 1 3 5 7
+            const float rx = __shfl_xor(odd ? x[0] : x[2], 32, 64);
+            const float ry = __shfl_xor(odd ? x[1] : x[3], 32, 64);
+            r = odd ? f32x4{rx, x[2], ry, x[3]} : f32x4{x[0], rx, x[1], ry};
+          } else {            // lower lane: channels 0 4 1 5, upper lane: 2 6 3 7
+            const float rx = __shfl_xor(odd ? x[0] : x[1], 32, 64);
+            const float ry = __shfl_xor(odd ? x[2] : x[3], 32, 64);
+            r = odd ? f32x4{rx, ry, x[1], x[3]} : f32x4{x[0], x[2], rx, ry};
+          }
+          *reinterpret_cast<f32x4*>(dh + 8 * (16 * v + 4 * cb + a) + 4 * half) = r;
         }
     }
     if (G < 2) {

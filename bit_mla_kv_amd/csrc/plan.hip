@@ -6,7 +6,8 @@
 // pages / target items), and every sequence gets one more item for its bf16
 // (sink + recent) tokens.  Items are ordered full chunks first, then the
 // shorter tail chunks, then the bf16 items, so the hardware's in-order
-// dispatch starts the longest work first.  combine_kernel merges each
+// dispatch starts the longest work first.  When a slightly longer chunk lets
+// every item run at once (one round of workgroups), that chunk is used.  combine_kernel merges each
 // sequence's partial results exactly (max-shifted sums), adding the deferred
 // zero terms, and writes bf16 outputs and natural-log lse.
 #include <algorithm>
@@ -18,6 +19,7 @@ namespace {
 using namespace dev;
 
 constexpr int kPlanThreads = 64;  // one wave: scans are lane shuffles, no workgroup barriers
+constexpr int kPlanRegs = 8;      // sequence lengths a lane keeps in registers for the chunk search
 
 __device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, int* first_page) {
   int N = p.seq_len[b];
@@ -54,6 +56,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   const long long total = local;
   int pps = (int)std::min<long long>((total + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
+  // target_items workgroups run at once.  Full chunks plus tails plus the bf16 items can exceed it
+  // by up to 2 x batch, and the excess then runs as a second round after a full chunk.  When a
+  // chunk at most a quarter longer brings every item into one round, take the shortest such chunk.
+  if (p.batch <= kPlanThreads * kPlanRegs && 2 * p.batch <= p.target_items) {
+    int n_reg[kPlanRegs];
+    int n_max = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanRegs; ++k) {
+      const int b = t + kPlanThreads * k;
+      int fp;
+      n_reg[k] = b < p.batch ? seq_packed_pages(p, b, &fp) : 0;
+      n_max = std::max(n_max, n_reg[k]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
+    auto items_at = [&](int c) {  // all items of a plan with chunks of c pages
+      int n = 0;
+#pragma unroll
+      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
+      return n + p.batch;
+    };
+    int lo = pps, hi = std::min(std::max(n_max, pps), pps + pps / 4);
+    if (items_at(lo) > p.target_items && items_at(hi) <= p.target_items) {
+      while (hi - lo > 1) {  // items_at(lo) > target_items >= items_at(hi); items_at is non-increasing
+        const int mid = lo + (hi - lo) / 2;
+        if (items_at(mid) <= p.target_items) hi = mid;
+        else lo = mid;
+      }
+      pps = hi;
+    }
+  }
   if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
 
   // pass 1: counts of full / tail items, scanned in chunks of 64 sequences (lane t owns sequence
