@@ -299,17 +299,25 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
           *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + 128 * g + 16)) = k1;
         }
       }
-      // Z and SV tile entries: lane (token L16, G) writes groups 2G, 2G + 1 (lanes G = 0 also z_8
-      // into column 8), then reads its zero-term operand back: z_0 .. z_7 (G < 2) or z_8 and zeros
+      // The token's zeros in fp16 (every lane holds its token's nine), the zero-term operand from
+      // them (z_0 .. z_7 for G < 2, z_8 and zeros for G >= 2), and the Z and SV tile entries: lanes
+      // G = 0 write the token's Z row, lane G writes the PV scales of groups 2G, 2G + 1.
+      f16x8 zlo;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) zlo[g] = (f16)bf16f(mw[g] >> 16);
+      const f16 z8 = (f16)bf16f(mw[8] >> 16);
+      const f16x8 zf = G < 2 ? zlo : f16x8{z8, 0, 0, 0, 0, 0, 0, 0};
       {
-        const uint32_t m0 = G == 0 ? mw[0] : G == 1 ? mw[2] : G == 2 ? mw[4] : mw[6];
-        const uint32_t m1 = G == 0 ? mw[1] : G == 1 ? mw[3] : G == 2 ? mw[5] : mw[7];
-        *reinterpret_cast<lds_ptr<f16x2>>(tb + (o_zwr + 4 * G)) = f16x2{(f16)bf16f(m0 >> 16), (f16)bf16f(m1 >> 16)};
+        const uint32_t a0 = (G & 1) ? mw[2] : mw[0], b0 = (G & 1) ? mw[6] : mw[4];
+        const uint32_t a1 = (G & 1) ? mw[3] : mw[1], b1 = (G & 1) ? mw[7] : mw[5];
+        const uint32_t m0 = (G & 2) ? b0 : a0, m1 = (G & 2) ? b1 : a1;
         *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G)) = (f16)bf16f(m0 & 0xFFFFu);
         *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G + 32)) = (f16)bf16f(m1 & 0xFFFFu);
-        if (G == 0) *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + 16)) = (f16)bf16f(mw[8] >> 16);
+        if (G == 0) {
+          *reinterpret_cast<lds_ptr<f16x8>>(tb + o_zwr) = zlo;
+          *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + 16)) = z8;
+        }
       }
-      const f16x8 zf = lds_load<f16x8>(tb + (o_zwr + 16 * (G >> 1)));
       return mfma32k(qz, zf, s * c_log2) + (valid ? 0.f : -__builtin_inff());
     };
 
@@ -328,8 +336,8 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < GE::CI; ++i) {
         const int sl = 64 * i + lane, tt = sl / GE::RS, u = sl % GE::RS;
-        cact[i] = tt < kB && u < GE::CU;
-        coff[i] = (16 * pr + tt) * GE::CB + 16 * u;
+        cact[i] = i < GE::CI - 1 || tt < kB;  // all lanes busy but in the last instruction
+        coff[i] = (16 * pr + tt) * GE::CB + 16 * min(u, GE::CU - 1);  // the padding slot repeats a unit
       }
       // block t (page page0 + min(t, last)) into zone t % 3; every block issues GE::LOADS instructions
       auto stage = [&](int t, int pg) {
@@ -339,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         // The destination goes through an empty asm so that the compiler does not tie these loads
         // to the staging array: its own waits would then hold every read of the array until all
         // staging loads land.  The explicit vmcnt wait before a block is read orders them instead.
+        // (called after the publish of block t - 3, whose wait covered every read of this zone)
         const lds_ptr<uint8_t> zone = lds_opaque(&s_stage[pr][t % kZones][0]);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of this zone are done
 #pragma unroll
         for (int i = 0; i < GE::CI; ++i)
           if (cact[i])
@@ -360,18 +368,22 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         const int zo = (pr * kZones + t % kZones) * GE::SZ;
         const int tok = (page0 + t) * kPageTokens + row;
         const bool valid = tok >= p_lo && tok < p_hi;
+        // every LDS read of the block is issued before any arithmetic (the scheduler would otherwise
+        // sink the metadata reads below the MFMAs and leave the scale FMAs to the end)
         uint32_t mw[kGroups];
+        u32x2 kv[kGroups];
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-          const uint32_t v = lds_load<uint32_t>(sb + (zo + o_m + 4 * g));
-          mw[g] = valid ? v : 0u;
+          // (vector types: a struct load can be split into loads that lose their object)
+          if (g == 8) kv[g] = lds_load<u32x2>(sb + (zo + o_r));
+          else if (BITS_C == 4) kv[g] = lds_load<u32x2>(sb + (zo + o_c + 32 * g));
+          else kv[g] = u32x2{lds_load<uint32_t>(sb + (zo + o_c + 16 * g)), 0u};
+          mw[g] = lds_load<uint32_t>(sb + (zo + o_m + 4 * g));
         }
-        // (vector types: a struct load can be split into loads that lose their object)
-        auto kw = [&](int g) -> u32x2 {
-          if (g == 8) return lds_load<u32x2>(sb + (zo + o_r));
-          if (BITS_C == 4) return lds_load<u32x2>(sb + (zo + o_c + 32 * g));
-          return u32x2{lds_load<uint32_t>(sb + (zo + o_c + 16 * g)), 0u};
-        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) mw[g] = valid ? mw[g] : 0u;
+        auto kw = [&](int g) -> u32x2 { return kv[g]; };
         auto none = [&](int, int) { return f16x8{}; };
         return block_qk(kw, none, mw, valid, true);
       };
@@ -388,17 +400,19 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GE::LOADS) : "memory");  // block t landed
           wait_at_least(fl + 1, t - 1);  // the PV wave has taken block t - 1's tiles
           S = produce(t);
-          stage(t + 3, pg_next);  // zone t % 3: block t's reads are done
-          pg_next = page_id(t + 4);
           if (needs_refresh(S)) {
             held = true;
             break;
           }
           publish(S, t, false);
+          stage(t + 3, pg_next);  // zone t % 3: block t's reads are done
+          pg_next = page_id(t + 4);
         }
         if (!held) break;
         refresh(S);  // rare: kept apart from the block loop
         publish(S, t, true);
+        stage(t + 3, pg_next);
+        pg_next = page_id(t + 4);
         ++t;
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no staging left in flight
