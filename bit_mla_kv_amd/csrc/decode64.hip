@@ -5,29 +5,28 @@
 // softmax over all valid tokens, sink / recent tokens from bf16, all others
 // from their packed copies, output aggregated over the content latent.
 //
-// One workgroup of 8 waves per (sequence, split, 64-head group), specialised
-// by role so that each wave keeps only its own long-lived registers.  The
-// shared LDS read bandwidth (128 B/clk/CU) is the binding resource, so the
-// roles are cut to keep LDS bytes per token low:
-//  - QK waves 0, 1 hold the queries of 32 heads each and score one 32-token
+// One workgroup of 8 waves per (sequence, split, 64-head group), one QK wave
+// and one PV wave on each SIMD, so that the MFMA and VALU work of a step is
+// spread evenly over the four SIMDs:
+//  - QK waves 0..3 hold the queries of 16 heads each and score one 32-token
 //    tile per step with MFMA 16x16x32 f16 (queries as the A operand, so each
 //    lane owns one token of a 16-token block and applies that token's fp32
-//    group scales as scalars; every tile operand read feeds two head blocks).
-//    The zero terms of all nine groups go through one more MFMA against the
-//    tile's zero columns with qsum split into fp16 hi + lo.  Online softmax in
-//    the log2 domain with a lazily refreshed running max; probabilities are
-//    published to LDS as fp16 [token][head];
-//  - unpack waves 2, 3 load the packed bytes of a tile from HBM into
-//    registers three steps ahead and unpack them into an fp16 tile of exact
-//    codes (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
-//    converted with a 2^9 scale) plus per-token scales, zeros and masks;
+//    group scales as scalars).  The zero terms of all nine groups go through
+//    one more MFMA against the tile's zero columns with qsum split into fp16
+//    hi + lo.  Online softmax in the log2 domain with a lazily refreshed
+//    running max; probabilities are published to LDS as fp16 [token][head].
+//    The same waves also load the packed bytes of the tile three steps ahead
+//    into registers (a quarter of the tile each) and unpack the next tile
+//    into an fp16 tile of exact codes (nibbles / crumbs become fp8 bytes whose
+//    e4m3 value is code * 2^-9, converted with a 2^9 scale) plus per-token
+//    scales, zeros and masks;
 //  - PV waves 4..7 hold the output of content groups 2v, 2v+1 (v = w - 4) for
 //    all 64 heads and accumulate p * s_g times the exact codes (MFMA 32x32x16
 //    f16, both operands read with the LDS transpose load) plus the zero-term
 //    sums sum_t p_t z_g,t.
 // Tiles flow through a three-slot LDS ring: in step k the QK waves score tile
-// k, the PV waves accumulate tile k - 1 and the unpack waves write tile k + 1;
-// one workgroup barrier per tile.
+// k and write tile k + 1, the PV waves accumulate tile k - 1; one workgroup
+// barrier per tile.
 // Partials are left unnormalised with their running max and sum; the combine
 // kernel adds the zero terms and merges splits.
 #include <algorithm>
@@ -42,7 +41,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kT = 32;            // tokens per tile (half a page)
 constexpr int kHW = 64;           // query heads per workgroup
-constexpr int kThreads = 512;     // 2 QK waves, 2 unpack waves, 4 PV waves
+constexpr int kThreads = 512;     // 4 QK + unpack waves, 4 PV waves
 constexpr int kSlots = 3;         // tile ring
 constexpr int kS = 592;           // tile row stride (halves): 576 codes + 16 zero-term columns
 constexpr int kZ = 576;           // zero-term columns: z_0..z_7, then z_8 and seven zeros
@@ -57,17 +56,18 @@ struct Geo {
   static constexpr int META0 = kPageTokens * (CB + kDr / 2);               // metadata block of a page
   static constexpr int CDW = kT * CB / 4;      // content dwords of a tile
   static constexpr int DPR = CB / 4;           // content dwords per token
-  static constexpr int CPT = CDW / 128;        // content dwords per unpack thread
-  static constexpr int RPT = kT * kDr / 8 / 128;  // RoPE dwords per unpack thread (2)
-  static_assert(CDW % 128 == 0 && RPT == 2, "unpack split assumes these sizes");
+  static constexpr int CPT = CDW / 256;        // content dwords per unpack thread
+  static constexpr int RPT = kT * kDr / 8 / 256;  // RoPE dwords per unpack thread (1)
+  static_assert(CDW % 256 == 0 && RPT == 1, "unpack split assumes these sizes");
 };
 
-// packed bytes of one tile held by an unpack thread (wave 2 lanes < 32 also carry one token's metadata)
+// packed bytes of one tile held by an unpack thread: content, RoPE, and the metadata words of
+// (token t % 32, group t / 32) and (token t % 32, group 8) for thread t
 template <int BITS_C>
 struct TileRegs {
   uint32_t c[Geo<BITS_C>::CPT];
-  uint32_t r[2];
-  uint3 m[3];
+  uint32_t r;
+  uint32_t m[2];
 };
 
 template <int BITS_C>
@@ -78,8 +78,7 @@ struct __align__(16) Smem64 {
   float bias[kSlots][kT];          // at sq_pos(token): 0 valid, -inf masked
   f16 svh[kSlots][8][kT];          // PV group scale s_g (fp16); 0 for masked tokens
   float alpha[2][kHW];             // per-head rescale factor for the PV accumulators
-  int resc[2][2];                  // per-QK-wave "some head was rescaled" flags
-  f16x8 qfrag[3][2][2][64];        // [RoPE step 0, RoPE step 1, zero-term step][QK wave][head block][lane]
+  int resc[2][4];                  // per-QK-wave "some head was rescaled" flags
 };
 
 // Per-token QK constants sit so that one 8-byte read gives a lane the values of its token in
@@ -166,215 +165,34 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   const float c_log2 = p.scale_log2e;
   const int64_t row0 = (int64_t)item * p.heads + head0;  // first workspace row of this workgroup
 
-  if (w < 2) {
-    // ====================== QK waves: heads head0 + 32w + 16hb + L16, hb = 0, 1 ======================
-    // queries: A operand of QK 16x16x32 (lane: head .. + L16, positions 32 ks + 8 G + j)
-    f16x8 qreg[2][16];  // content K steps; the RoPE steps and the zero-term step live in LDS
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float qs[kGroups];
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) qs[g] = 0.f;
-      const uint16_t* qh = p.q + ((int64_t)b * p.heads + head0 + 32 * w + 16 * hb + L16) * kD;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(qh + 32 * ks + 8 * G);
-        const uint4 hv = ks < 16 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw);
-        const f16x8 fr = __builtin_bit_cast(f16x8, hv);
-        if (ks < 16) qreg[hb][ks] = fr;
-        else sm.qfrag[ks - 16][w][hb][lane] = fr;
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sum += (float)fr[j];
-        qs[ks < 16 ? ks / 2 : 8] += sum;
-      }
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        qs[g] += __shfl_xor(qs[g], 16, 64);
-        qs[g] += __shfl_xor(qs[g], 32, 64);
-        qs[g] *= c_log2;
-      }
-      // zero-term step, k = 8 G + j: G0 hi(qsum_j), G1 lo(qsum_j) against z_j; G2 / G3 hi / lo of
-      // qsum_8 in slot j = 0 against z_8 (the other slots meet zero columns)
-      f16x8 z;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = G < 2 ? qs[j] : (j == 0 ? qs[8] : 0.f);
-        const f16 hi = (f16)x;
-        const f16 lo = (f16)(x - (float)hi);
-        z[j] = (G & 1) ? lo : hi;
-      }
-      sm.qfrag[2][w][hb][lane] = z;
-    }
-    float m_run[2][4], l_part[2][4];  // heads .. + 16hb + 4G + i (the lane's D rows)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        m_run[hb][i] = -__builtin_inff();
-        l_part[hb][i] = 0.f;
-      }
-    __syncthreads();  // first tile unpacked, query fragments visible
-
-    for (int k = 0; k < n_steps; ++k) {
-      if (k < n_tiles) {
-        const int sl = k % kSlots, pb = k & 1;
-        const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
-        const lds_ptr<f16x8> qf = lds_opaque(&sm.qfrag[0][w][0][lane]);  // + 256 step + 64 hb
-        // lane (token L16 of each 16-token block, heads .. + 16hb + 4G + i)
-        f32x4 S[2][2];
-        {
-          const lds_ptr<float> sqp = lds_opaque(&sm.sq[sl][0][0]) + 2 * L16;
-          const lds_ptr<f16> k0 = tb + L16 * kS + 8 * G;
-          const lds_ptr<f16> k1 = k0 + 16 * kS;
-          f32x4 s[2][2];
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // software pipeline: the tile operands and scales of group g + kAhead are requested
-          // before group g multiplies (the scheduling fences keep the requests in place)
-          constexpr int kAhead = 2;
-          f16x8 kf[kAhead][4];
-          f32x2 scf[kAhead];
-          auto request = [&](int g) {
-            kf[g % kAhead][0] = lds_load<f16x8>(k0 + 64 * g);
-            kf[g % kAhead][1] = lds_load<f16x8>(k1 + 64 * g);
-            kf[g % kAhead][2] = lds_load<f16x8>(k0 + 64 * g + 32);
-            kf[g % kAhead][3] = lds_load<f16x8>(k1 + 64 * g + 32);
-            scf[g % kAhead] = lds_load<f32x2>(sqp + g * kT);
-          };
-#pragma unroll
-          for (int g = 0; g < kAhead; ++g) request(g);
-#pragma unroll
-          for (int g = 0; g < kGroups; ++g) {
-            const int r = g % kAhead;
-            f32x4 c[2][2];
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-              const f16x8 q0 = g < 8 ? qreg[hb][2 * g] : lds_load<f16x8>(qf + 64 * hb);
-              const f16x8 q1 = g < 8 ? qreg[hb][2 * g + 1] : lds_load<f16x8>(qf + 256 + 64 * hb);
-              const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-              c[hb][0] = mfma16(q0, kf[r][0], z4);
-              c[hb][1] = mfma16(q0, kf[r][1], z4);
-              c[hb][0] = mfma16(q1, kf[r][2], c[hb][0]);
-              c[hb][1] = mfma16(q1, kf[r][3], c[hb][1]);
-            }
-            const f32x2 sc = scf[r];
-            __builtin_amdgcn_sched_barrier(0);
-            if (g + kAhead < kGroups) request(g + kAhead);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-              s[hb][0] += sc[0] * c[hb][0];
-              s[hb][1] += sc[1] * c[hb][1];
-            }
-          }
-          // zero terms of all nine groups
-          const int zc = kZ + 8 * (G >> 1);
-          const f16x8 zr0 = lds_load<f16x8>(tb + L16 * kS + zc);
-          const f16x8 zr1 = lds_load<f16x8>(tb + (16 + L16) * kS + zc);
-          const f32x2 bv = lds_load<f32x2>(lds_opaque(&sm.bias[sl][0]) + 2 * L16);
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const f16x8 qz = lds_load<f16x8>(qf + 512 + 64 * hb);
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-            S[hb][0] = s[hb][0] + mfma16(qz, zr0, z4) + bv[0];
-            S[hb][1] = s[hb][1] + mfma16(qz, zr1, z4) + bv[1];
-          }
-        }
-        // online softmax; a head's running max is refreshed only when one of its scores
-        // exceeds it by more than kRescale
-        bool need = false;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            need |= (S[hb][0][i] > m_run[hb][i] + kRescale) | (S[hb][1][i] > m_run[hb][i] + kRescale);
-        const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-        float alpha[2][4];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) alpha[hb][i] = 1.f;
-        if (any) {
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float mx = row16_max(fmaxf(S[hb][0][i], S[hb][1][i]));
-              const float m_new = fmaxf(m_run[hb][i], mx);
-              alpha[hb][i] = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[hb][i] - m_new);
-              m_run[hb][i] = m_new;
-              l_part[hb][i] *= alpha[hb][i];
-            }
-        }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          f16x4 pz[2];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float mu = m_run[hb][i] == -__builtin_inff() ? 0.f : m_run[hb][i];
-            const float e0 = __builtin_amdgcn_exp2f(S[hb][0][i] - mu);
-            const float e1 = __builtin_amdgcn_exp2f(S[hb][1][i] - mu);
-            l_part[hb][i] += e0 + e1;
-            pz[0][i] = (f16)e0;
-            pz[1][i] = (f16)e1;
-          }
-          const int hc = 32 * w + 16 * hb + 4 * G;  // first head column of the lane's rows
-          f16* prow = &sm.probT[pb][L16][hc];
-          *reinterpret_cast<f16x4*>(prow) = pz[0];
-          *reinterpret_cast<f16x4*>(prow + 16 * kPT) = pz[1];
-          if (L16 == 0)
-            *reinterpret_cast<f32x4*>(&sm.alpha[pb][hc]) = f32x4{alpha[hb][0], alpha[hb][1], alpha[hb][2], alpha[hb][3]};
-        }
-        if (lane == 0) sm.resc[pb][w] = any ? 1 : 0;
-      }
-      __syncthreads();
-    }
-    // running max and sum of the heads of this wave
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float l_tot = row16_sum(l_part[hb][i]);
-        if (L16 == 0) {
-          const int64_t hrow = row0 + 32 * w + 16 * hb + 4 * G + i;
-          p.ws_ml[2 * hrow] = m_run[hb][i];
-          p.ws_ml[2 * hrow + 1] = l_tot;
-        }
-      }
-  } else if (w < 4) {
-    // =========================== unpack waves: tiles into the LDS ring ===========================
-    const int ft = tid - 128;  // 0 .. 127
-    const bool meta_lane = ft < kT;  // wave 2, lanes 0 .. 31: metadata of token ft
-    const int64_t slot_row = (int64_t)slot * p.max_pages;
+  if (w < 4) {
+    // ====== QK + unpack waves: QK of heads head0 + 16w + L16, unpacking of a quarter of each tile ======
+    const int ft = tid;  // 0 .. 255
+    typedef __attribute__((address_space(4))) const int32_t cint;
+    cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
     // packed bytes of tile min(t, n_tiles - 1) (half t % 2 of page page0 + t / 2) into registers;
     // every call issues the same loads, so the compiler's load counting stays exact
     auto load = [&](int t, TileRegs<BITS_C>& R) {
       t = min(t, n_tiles - 1);
       const int page_idx = page0 + (t >> 1), hs = t & 1;
-      int64_t pg = (page_idx < p.max_pages) ? (int64_t)scalar_load(p.block_table + slot_row + page_idx) : 0;
+      int64_t pg = (page_idx < p.max_pages) ? (int64_t)bt[min(page_idx, p.max_pages - 1)] : 0;
       if (pg < 0 || pg >= p.num_pages) pg = 0;  // contract violation: wrong values, no fault
       const uint8_t* base = p.pages + pg * (int64_t)GE::PB;
       const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + hs * kT * GE::CB);
       const uint32_t* srcR = reinterpret_cast<const uint32_t*>(base + GE::ROPE0 + hs * kT * kDr / 2);
+      const uint32_t* srcM = reinterpret_cast<const uint32_t*>(base + GE::META0 + hs * kT * 4 * kGroups);
 #pragma unroll
-      for (int i = 0; i < GE::CPT; ++i) R.c[i] = srcC[ft + 128 * i];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) R.r[i] = srcR[ft + 128 * i];
-      if (w == 2) {
-        const uint3* srcM = reinterpret_cast<const uint3*>(base + GE::META0 + hs * kT * 4 * kGroups) + 3 * min(ft, kT - 1);
-        if (meta_lane) {
-#pragma unroll
-          for (int i = 0; i < 3; ++i) R.m[i] = srcM[i];
-        }
-      }
+      for (int i = 0; i < GE::CPT; ++i) R.c[i] = srcC[ft + 256 * i];
+      R.r = srcR[ft];
+      R.m[0] = srcM[(ft & 31) * kGroups + (ft >> 5)];
+      R.m[1] = srcM[(ft & 31) * kGroups + 8];
     };
     // unpack tile t into ring slot t % 3
     auto fill = [&](int t, const TileRegs<BITS_C>& R) {
       const int sl = t % kSlots;
       f16* tile = &sm.tile[sl][0];
       if (!packed) {
-        for (int e = ft; e < kT * (kD / 8); e += 128) {
+        for (int e = ft; e < kT * (kD / 8); e += 256) {
           const int r = e / (kD / 8), m = e % (kD / 8);
           const int j = t * kT + r;
           uint4 o = make_uint4(0, 0, 0, 0);
@@ -391,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           }
           *reinterpret_cast<uint4*>(&tile[r * kS + 8 * m]) = o;
         }
-        if (meta_lane) {
+        if (ft < kT) {
           const int r = ft;
           const bool valid = t * kT + r < nb;
 #pragma unroll
@@ -407,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       // content codes: consecutive lanes write consecutive 16-byte (C4) or 32-byte (C2) runs
 #pragma unroll
       for (int i = 0; i < GE::CPT; ++i) {
-        const int u = ft + 128 * i;
+        const int u = ft + 256 * i;
         const int r = u / GE::DPR, d = u % GE::DPR;
         f16* dst = &tile[r * kS];
         if (BITS_C == 4) {
@@ -419,49 +237,168 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           *reinterpret_cast<uint4*>(dst + 16 * d + 8) = x1;
         }
       }
-      // RoPE-key codes: dword u holds channels 8 (u % 8) .. +7 of token u / 8
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int u = ft + 128 * i;
-        *reinterpret_cast<uint4*>(&tile[(u >> 3) * kS + kDc + 8 * (u & 7)]) = unpack4(R.r[i]);
+      // RoPE-key codes: dword ft holds channels 8 (ft % 8) .. +7 of token ft / 8
+      *reinterpret_cast<uint4*>(&tile[(ft >> 3) * kS + kDc + 8 * (ft & 7)]) = unpack4(R.r);
+      // metadata (s | z << 16) of token r = ft % 32: group ft / 32, and group 8 for threads < 32
+      const int r = ft & 31;
+      const int tok = (page0 + (t >> 1)) * kPageTokens + (t & 1) * kT + r;
+      const bool valid = tok >= p_lo && tok < p_hi;
+      {
+        const int g = ft >> 5;
+        const float sc = valid ? bf16f(R.m[0] & 0xFFFFu) : 0.f;
+        sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
+        sm.svh[sl][g][r] = (f16)sc;
+        tile[r * kS + kZ + g] = (f16)(valid ? bf16f(R.m[0] >> 16) : 0.f);
+        if (g == 0) sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
       }
-      if (meta_lane) {  // metadata of token ft: (s | z << 16) for the nine groups
-        const int r = ft;
-        const uint32_t md[kGroups] = {R.m[0].x, R.m[0].y, R.m[0].z, R.m[1].x, R.m[1].y,
-                                      R.m[1].z, R.m[2].x, R.m[2].y, R.m[2].z};
-        const int tok = (page0 + (t >> 1)) * kPageTokens + (t & 1) * kT + r;
-        const bool valid = tok >= p_lo && tok < p_hi;
-        f16 zh[kGroups];
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          const float sc = valid ? bf16f(md[g] & 0xFFFFu) : 0.f;
-          zh[g] = (f16)(valid ? bf16f(md[g] >> 16) : 0.f);
-          sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
-          if (g < 8) sm.svh[sl][g][r] = (f16)sc;
-        }
-        uint4 z0;
-        z0.x = __builtin_bit_cast(uint32_t, f16x2{zh[0], zh[1]});
-        z0.y = __builtin_bit_cast(uint32_t, f16x2{zh[2], zh[3]});
-        z0.z = __builtin_bit_cast(uint32_t, f16x2{zh[4], zh[5]});
-        z0.w = __builtin_bit_cast(uint32_t, f16x2{zh[6], zh[7]});
-        *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = z0;
+      if (ft < kT) {
+        const float sc = valid ? bf16f(R.m[1] & 0xFFFFu) : 0.f;
+        sm.sq[sl][8][sq_pos(r)] = sc * c_log2;
+        const f16 z8 = (f16)(valid ? bf16f(R.m[1] >> 16) : 0.f);
         *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
-            make_uint4(__builtin_bit_cast(uint32_t, f16x2{zh[8], (f16)0.f}), 0, 0, 0);
-        sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
+            make_uint4(__builtin_bit_cast(uint32_t, f16x2{z8, (f16)0.f}), 0, 0, 0);
       }
     };
+
+    // queries: A operand of QK 16x16x32 (lane: head head0 + 16w + L16, positions 32 ks + 8 G + j)
+    f16x8 qreg[18];
+    f16x8 qz;
+    auto load_queries = [&]() {
+      float qs[kGroups];
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) qs[g] = 0.f;
+      const uint16_t* qh = p.q + ((int64_t)b * p.heads + head0 + 16 * w + L16) * kD;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(qh + 32 * ks + 8 * G);
+        const uint4 hv = ks < 16 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw);
+        qreg[ks] = __builtin_bit_cast(f16x8, hv);
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += (float)qreg[ks][j];
+        qs[ks < 16 ? ks / 2 : 8] += sum;
+      }
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        qs[g] += __shfl_xor(qs[g], 16, 64);
+        qs[g] += __shfl_xor(qs[g], 32, 64);
+        qs[g] *= c_log2;
+      }
+      // zero-term step, k = 8 G + j: G0 hi(qsum_j), G1 lo(qsum_j) against z_j; G2 / G3 hi / lo of
+      // qsum_8 in slot j = 0 against z_8 (the other slots meet zero columns)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = G < 2 ? qs[j] : (j == 0 ? qs[8] : 0.f);
+        const f16 hi = (f16)x;
+        const f16 lo = (f16)(x - (float)hi);
+        qz[j] = (G & 1) ? lo : hi;
+      }
+    };
+    float m_run[4], l_part[4];  // heads .. + 4G + i (the lane's D rows)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m_run[i] = -__builtin_inff();
+      l_part[i] = 0.f;
+    }
+    // QK and softmax of tile k; probabilities to probT[k % 2]
+    auto qk_step = [&](int k) {
+      if (k >= n_tiles) return;
+      const int sl = k % kSlots, pb = k & 1;
+      const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
+      // lane (token L16 of each 16-token block, heads .. + 4G + i)
+      f32x4 S[2];
+      {
+        const lds_ptr<float> sqp = lds_opaque(&sm.sq[sl][0][0]) + 2 * L16;
+        const lds_ptr<f16> k0 = tb + L16 * kS + 8 * G;
+        const lds_ptr<f16> k1 = k0 + 16 * kS;
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        // software pipeline: the tile operands and scales of group g + kAhead are requested
+        // before group g multiplies (the scheduling fences keep the requests in place)
+        constexpr int kAhead = 3;
+        f16x8 kf[kAhead][4];
+        f32x2 scf[kAhead];
+        auto request = [&](int g) {
+          kf[g % kAhead][0] = lds_load<f16x8>(k0 + 64 * g);
+          kf[g % kAhead][1] = lds_load<f16x8>(k1 + 64 * g);
+          kf[g % kAhead][2] = lds_load<f16x8>(k0 + 64 * g + 32);
+          kf[g % kAhead][3] = lds_load<f16x8>(k1 + 64 * g + 32);
+          scf[g % kAhead] = lds_load<f32x2>(sqp + g * kT);
+        };
+#pragma unroll
+        for (int g = 0; g < kAhead; ++g) request(g);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+          const int r = g % kAhead;
+          const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+          f32x4 c0 = mfma16(qreg[2 * g], kf[r][0], z4);
+          f32x4 c1 = mfma16(qreg[2 * g], kf[r][1], z4);
+          c0 = mfma16(qreg[2 * g + 1], kf[r][2], c0);
+          c1 = mfma16(qreg[2 * g + 1], kf[r][3], c1);
+          const f32x2 sc = scf[r];
+          __builtin_amdgcn_sched_barrier(0);
+          if (g + kAhead < kGroups) request(g + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
+          s[0] += sc[0] * c0;
+          s[1] += sc[1] * c1;
+        }
+        // zero terms of all nine groups
+        const int zc = kZ + 8 * (G >> 1);
+        const f16x8 zr0 = lds_load<f16x8>(tb + L16 * kS + zc);
+        const f16x8 zr1 = lds_load<f16x8>(tb + (16 + L16) * kS + zc);
+        const f32x2 bv = lds_load<f32x2>(lds_opaque(&sm.bias[sl][0]) + 2 * L16);
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        S[0] = s[0] + mfma16(qz, zr0, z4) + bv[0];
+        S[1] = s[1] + mfma16(qz, zr1, z4) + bv[1];
+      }
+      // online softmax; a head's running max is refreshed only when one of its scores
+      // exceeds it by more than kRescale
+      bool need = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) need |= (S[0][i] > m_run[i] + kRescale) | (S[1][i] > m_run[i] + kRescale);
+      const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+      float alpha[4] = {1.f, 1.f, 1.f, 1.f};
+      if (any) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float mx = row16_max(fmaxf(S[0][i], S[1][i]));
+          const float m_new = fmaxf(m_run[i], mx);
+          alpha[i] = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+          m_run[i] = m_new;
+          l_part[i] *= alpha[i];
+        }
+      }
+      f16x4 pz[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mu = m_run[i] == -__builtin_inff() ? 0.f : m_run[i];
+        const float e0 = __builtin_amdgcn_exp2f(S[0][i] - mu);
+        const float e1 = __builtin_amdgcn_exp2f(S[1][i] - mu);
+        l_part[i] += e0 + e1;
+        pz[0][i] = (f16)e0;
+        pz[1][i] = (f16)e1;
+      }
+      const int hc = 16 * w + 4 * G;  // first head column of the lane's rows
+      f16* prow = &sm.probT[pb][L16][hc];
+      *reinterpret_cast<f16x4*>(prow) = pz[0];
+      *reinterpret_cast<f16x4*>(prow + 16 * kPT) = pz[1];
+      if (L16 == 0) *reinterpret_cast<f32x4*>(&sm.alpha[pb][hc]) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
+      if (lane == 0) sm.resc[pb][w] = any ? 1 : 0;
+    };
+
     if (packed) {
-      // tile t lives in R(t % 3); step k requests tile k + 3 into the registers tile k held and
-      // unpacks tile k + 1 (the waits for its loads, two batches deep, come from the compiler)
+      // tile t lives in R(t % 3); step k requests tile k + 3 into the registers tile k held, scores
+      // tile k and unpacks tile k + 1 (the waits for its loads, two batches deep, come from the compiler)
       TileRegs<BITS_C> R0, R1, R2;
       auto step = [&](int k, TileRegs<BITS_C>& next, const TileRegs<BITS_C>& cur) {
         load(k + 3, next);
+        qk_step(k);
         if (k + 1 < n_tiles) fill(k + 1, cur);
         __syncthreads();
       };
       load(0, R0);
       load(1, R1);
       load(2, R2);
+      load_queries();
       fill(0, R0);
       __syncthreads();  // first tile unpacked
       for (int k = 0; k < n_steps; k += 3) {
@@ -472,11 +409,23 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
     } else {
       const TileRegs<BITS_C> none{};
+      load_queries();
       if (n_tiles > 0) fill(0, none);
       __syncthreads();  // first tile unpacked
       for (int k = 0; k < n_steps; ++k) {
+        qk_step(k);
         if (k + 1 < n_tiles) fill(k + 1, none);
         __syncthreads();
+      }
+    }
+    // running max and sum of the heads of this wave
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l_tot = row16_sum(l_part[i]);
+      if (L16 == 0) {
+        const int64_t hrow = row0 + 16 * w + 4 * G + i;
+        p.ws_ml[2 * hrow] = m_run[i];
+        p.ws_ml[2 * hrow + 1] = l_tot;
       }
     }
   } else {
@@ -496,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         const int sl = (k - 1) % kSlots, pb = (k - 1) & 1;
         const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
         const lds_ptr<int> rf = lds_opaque(&sm.resc[pb][0]);
-        if (rf[0] | rf[1]) {
+        if (rf[0] | rf[1] | rf[2] | rf[3]) {
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             const float a = sm.alpha[pb][32 * hb + l32];
