@@ -16,14 +16,15 @@
 //    hi + lo.  Online softmax in the log2 domain with a lazily refreshed
 //    running max; probabilities are published to LDS as fp16 [token][head].
 //    The same waves also load the packed bytes of the tile three steps ahead
-//    into registers (a quarter of the tile each) and unpack the next tile
-//    into an fp16 tile of exact codes (nibbles / crumbs become fp8 bytes whose
-//    e4m3 value is code * 2^-9, converted with a 2^9 scale) plus per-token
-//    scales, zeros and masks;
+//    into registers and unpack the next tile into an fp16 tile of exact codes
+//    (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
+//    converted with a 2^9 scale) plus per-token scales, zeros and masks; they
+//    take half of the content codes, the RoPE-key codes and the metadata;
 //  - PV waves 4..7 hold the output of content groups 2v, 2v+1 (v = w - 4) for
 //    all 64 heads and accumulate p * s_g times the exact codes (MFMA 32x32x16
 //    f16, both operands read with the LDS transpose load) plus the zero-term
-//    sums sum_t p_t z_g,t.
+//    sums sum_t p_t z_g,t.  They load and unpack the other half of the
+//    content codes, so both roles of a SIMD share the unpacking work.
 // Tiles flow through a three-slot LDS ring: in step k the QK waves score tile
 // k and write tile k + 1, the PV waves accumulate tile k - 1; one workgroup
 // barrier per tile.
@@ -56,7 +57,8 @@ struct Geo {
   static constexpr int META0 = kPageTokens * (CB + kDr / 2);               // metadata block of a page
   static constexpr int CDW = kT * CB / 4;      // content dwords of a tile
   static constexpr int DPR = CB / 4;           // content dwords per token
-  static constexpr int CPT = CDW / 256;        // content dwords per unpack thread
+  static constexpr int CPT = CDW / 256;        // content dwords per thread index (QK and PV threads share them)
+  static constexpr int CQ = CPT / 2;           // content dwords a QK thread unpacks; a PV thread takes the rest
   static constexpr int RPT = kT * kDr / 8 / 256;  // RoPE dwords per unpack thread (1)
   static_assert(CDW % 256 == 0 && RPT == 1, "unpack split assumes these sizes");
 };
@@ -65,10 +67,44 @@ struct Geo {
 // (token t % 32, group t / 32) and (token t % 32, group 8) for thread t
 template <int BITS_C>
 struct TileRegs {
-  uint32_t c[Geo<BITS_C>::CPT];
+  uint32_t c[Geo<BITS_C>::CQ];
   uint32_t r;
   uint32_t m[2];
 };
+// the content dwords of a tile a PV thread loads and unpacks
+template <int BITS_C>
+struct PVRegs {
+  uint32_t c[Geo<BITS_C>::CPT - Geo<BITS_C>::CQ];
+};
+
+// Page id of page_idx of the slot's block table, read through the constant address space (scalar
+// loads); an index or id outside the table or the pool reads page 0 (wrong values, no fault).
+typedef __attribute__((address_space(4))) const int32_t cint;
+__device__ __forceinline__ int64_t page_of(const DecodeParams& p, cint* bt, int page_idx) {
+  int64_t pg = (page_idx < p.max_pages) ? (int64_t)bt[min(page_idx, p.max_pages - 1)] : 0;
+  if (pg < 0 || pg >= p.num_pages) pg = 0;
+  return pg;
+}
+
+// content dwords u = ft + 256 i (i in [I0, I0 + n)) of a tile: unpacked into the tile rows
+template <int BITS_C, int I0, int NI>
+__device__ __forceinline__ void unpack_content(f16* tile, int ft, const uint32_t (&c)[NI]) {
+  using GE = Geo<BITS_C>;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int u = ft + 256 * (I0 + i);
+    const int r = u / GE::DPR, d = u % GE::DPR;
+    f16* dst = &tile[r * kS];
+    if (BITS_C == 4) {
+      *reinterpret_cast<uint4*>(dst + 8 * d) = unpack4(c[i]);
+    } else {
+      uint4 x0, x1;
+      unpack2(c[i], x0, x1);
+      *reinterpret_cast<uint4*>(dst + 16 * d) = x0;
+      *reinterpret_cast<uint4*>(dst + 16 * d + 8) = x1;
+    }
+  }
+}
 
 template <int BITS_C>
 struct __align__(16) Smem64 {
@@ -168,21 +204,18 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   if (w < 4) {
     // ====== QK + unpack waves: QK of heads head0 + 16w + L16, unpacking of a quarter of each tile ======
     const int ft = tid;  // 0 .. 255
-    typedef __attribute__((address_space(4))) const int32_t cint;
     cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
     // packed bytes of tile min(t, n_tiles - 1) (half t % 2 of page page0 + t / 2) into registers;
     // every call issues the same loads, so the compiler's load counting stays exact
     auto load = [&](int t, TileRegs<BITS_C>& R) {
       t = min(t, n_tiles - 1);
-      const int page_idx = page0 + (t >> 1), hs = t & 1;
-      int64_t pg = (page_idx < p.max_pages) ? (int64_t)bt[min(page_idx, p.max_pages - 1)] : 0;
-      if (pg < 0 || pg >= p.num_pages) pg = 0;  // contract violation: wrong values, no fault
-      const uint8_t* base = p.pages + pg * (int64_t)GE::PB;
+      const int hs = t & 1;
+      const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1)) * (int64_t)GE::PB;
       const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + hs * kT * GE::CB);
       const uint32_t* srcR = reinterpret_cast<const uint32_t*>(base + GE::ROPE0 + hs * kT * kDr / 2);
       const uint32_t* srcM = reinterpret_cast<const uint32_t*>(base + GE::META0 + hs * kT * 4 * kGroups);
 #pragma unroll
-      for (int i = 0; i < GE::CPT; ++i) R.c[i] = srcC[ft + 256 * i];
+      for (int i = 0; i < GE::CQ; ++i) R.c[i] = srcC[ft + 256 * i];
       R.r = srcR[ft];
       R.m[0] = srcM[(ft & 31) * kGroups + (ft >> 5)];
       R.m[1] = srcM[(ft & 31) * kGroups + 8];
@@ -222,21 +255,9 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         }
         return;
       }
-      // content codes: consecutive lanes write consecutive 16-byte (C4) or 32-byte (C2) runs
-#pragma unroll
-      for (int i = 0; i < GE::CPT; ++i) {
-        const int u = ft + 256 * i;
-        const int r = u / GE::DPR, d = u % GE::DPR;
-        f16* dst = &tile[r * kS];
-        if (BITS_C == 4) {
-          *reinterpret_cast<uint4*>(dst + 8 * d) = unpack4(R.c[i]);
-        } else {
-          uint4 x0, x1;
-          unpack2(R.c[i], x0, x1);
-          *reinterpret_cast<uint4*>(dst + 16 * d) = x0;
-          *reinterpret_cast<uint4*>(dst + 16 * d + 8) = x1;
-        }
-      }
+      // content codes (this thread's share): consecutive lanes write consecutive 16-byte (C4) or
+      // 32-byte (C2) runs
+      unpack_content<BITS_C, 0, GE::CQ>(tile, ft, R.c);
       // RoPE-key codes: dword ft holds channels 8 (ft % 8) .. +7 of token ft / 8
       *reinterpret_cast<uint4*>(&tile[(ft >> 3) * kS + kDc + 8 * (ft & 7)]) = unpack4(R.r);
       // metadata (s | z << 16) of token r = ft % 32: group ft / 32, and group 8 for threads < 32
@@ -437,11 +458,9 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) O[hb][cb] = f32x16{};
-    __syncthreads();  // first tile unpacked
-
-    for (int k = 0; k < n_steps; ++k) {
+    // accumulate tile k - 1 (ring slot (k - 1) % 3, probabilities of step k - 1)
+    auto pv_step = [&](int k) {
       if (k >= 1 && k <= n_tiles) {
-        // accumulate tile k - 1 (ring slot (k - 1) % 3, probabilities of step k - 1)
         const int sl = (k - 1) % kSlots, pb = (k - 1) & 1;
         const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
         const lds_ptr<int> rf = lds_opaque(&sm.resc[pb][0]);
@@ -492,7 +511,47 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
             }
           }
       }
-      __syncthreads();
+    };
+
+    if (packed) {
+      // the PV threads load and unpack the content dwords the QK threads leave (same three-tile
+      // register ring: step k requests tile k + 3, accumulates tile k - 1, unpacks tile k + 1)
+      const int pt = tid - 256;
+      cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
+      auto pload = [&](int t, PVRegs<BITS_C>& R) {
+        t = min(t, n_tiles - 1);
+        const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1)) * (int64_t)GE::PB;
+        const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + (t & 1) * kT * GE::CB);
+#pragma unroll
+        for (int i = 0; i < GE::CPT - GE::CQ; ++i) R.c[i] = srcC[pt + 256 * (GE::CQ + i)];
+      };
+      auto pfill = [&](int t, const PVRegs<BITS_C>& R) {
+        unpack_content<BITS_C, GE::CQ, GE::CPT - GE::CQ>(&sm.tile[t % kSlots][0], pt, R.c);
+      };
+      auto step = [&](int k, PVRegs<BITS_C>& next, const PVRegs<BITS_C>& cur) {
+        pload(k + 3, next);
+        pv_step(k);
+        if (k + 1 < n_tiles) pfill(k + 1, cur);
+        __syncthreads();
+      };
+      PVRegs<BITS_C> R0, R1, R2;
+      pload(0, R0);
+      pload(1, R1);
+      pload(2, R2);
+      pfill(0, R0);
+      __syncthreads();  // first tile unpacked
+      for (int k = 0; k < n_steps; k += 3) {
+        step(k, R0, R1);
+        step(k + 1, R1, R2);
+        step(k + 2, R2, R0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
+    } else {
+      __syncthreads();  // first tile unpacked
+      for (int k = 0; k < n_steps; ++k) {
+        pv_step(k);
+        __syncthreads();
+      }
     }
     // unnormalised partial output and zero-term sums.  Registers 4a .. 4a + 3 of lanes l and l ^ 32
     // hold the 8 channels 8 (16 v + 4 cb + a) + 0..7 between them, in the unpacking order; each
