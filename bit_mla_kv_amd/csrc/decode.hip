@@ -9,8 +9,9 @@
 // every other token from its packed copy, unpacked inside the loop.
 //
 // Work decomposition: one workgroup per (sequence, split, head group).
-// Split 0 holds the bf16 tokens; splits 1.. hold page-aligned chunks of the
-// packed range (plan_kernel sizes them from the device-resident lengths).
+// Some splits hold page-aligned chunks of the packed range, the others chunks
+// of the bf16 token list (plan_kernel sizes both from the device-resident
+// lengths).
 // Each split leaves an unnormalised partial output with its running max and
 // sum, and the zero-term sums; combine_kernel merges them exactly.
 //
@@ -26,7 +27,6 @@
 namespace mla {
 
 bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_len, DecodeConfig* cfg) {
-  (void)n_sink;
   if (heads > 0 && heads % 64 != 0 && heads % 16 == 0) {
     cfg->heads_per_wg = 16; cfg->threads = 256; cfg->wg_per_cu = 1;
   } else if (heads > 0 && heads % 64 == 0) {
@@ -53,14 +53,15 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
     const long v = strtol(env, nullptr, 10);
     if (v > 0) cfg->force_pages_per_split = (int)std::min<long>(v, 1 << 20);
   }
+  // per sequence: packed pages, and bf16 tokens in 64-token pages (at least one bf16 item each)
   const int64_t max_pp = std::max<int64_t>(0, ((int64_t)max_seq_len - n_recent + kPageTokens - 1) / kPageTokens);
-  int64_t packed_items;
-  if (cfg->force_pages_per_split > 0)
-    packed_items = (int64_t)batch * ((max_pp + cfg->force_pages_per_split - 1) / cfg->force_pages_per_split);
-  else  // full chunks <= total / chunk <= target, plus at most one tail chunk per sequence
-    packed_items = std::min<int64_t>((int64_t)batch * ((max_pp + cfg->min_pages_per_split - 1) / cfg->min_pages_per_split),
-                                     cfg->target_items + (int64_t)batch);
-  cfg->max_items = (int)std::min<int64_t>(packed_items + batch, 1 << 30);
+  const int64_t max_bp = ((int64_t)bf16_token_count(max_seq_len, n_sink, n_recent) + kPageTokens - 1) / kPageTokens;
+  const int64_t min_chunk = cfg->force_pages_per_split > 0 ? cfg->force_pages_per_split : cfg->min_pages_per_split;
+  int64_t items = (int64_t)batch * ((max_pp + min_chunk - 1) / min_chunk + std::max<int64_t>(1, (max_bp + min_chunk - 1) / min_chunk));
+  // full chunks (packed and bf16) <= total pages / chunk <= target, plus at most one packed tail
+  // and one short or empty bf16 item per sequence
+  if (cfg->force_pages_per_split <= 0) items = std::min<int64_t>(items, cfg->target_items + 2 * (int64_t)batch);
+  cfg->max_items = (int)std::min<int64_t>(items, 1 << 30);
   return true;
 }
 

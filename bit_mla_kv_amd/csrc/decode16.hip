@@ -149,12 +149,15 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   const int p_lo = p.n_sink, p_hi = N - p.n_recent;
   const int first_page = p_lo / kPageTokens;
   const int n_pp = p_hi > p_lo ? (p_hi - 1) / kPageTokens - first_page + 1 : 0;
-  int n_blocks, page0 = 0, ns = 0, nb = 0, rstart = 0;  // n_blocks: the pair's 16-token blocks
+  // n_blocks: the pair's 16-token blocks.  A bf16 item holds entries [jb, nb) of the sequence's
+  // bf16 token list (sink tokens, then the recent window from rstart on), in virtual pages of 64.
+  int n_blocks, page0 = 0, ns = 0, nb = 0, rstart = 0, jb = 0;
   if (!packed) {
     ns = min(p.n_sink, N);
     rstart = max(p.n_sink, N - p.n_recent);
-    nb = ns + max(0, N - rstart);
-    n_blocks = (nb + kPageTokens - 1) / kPageTokens;  // bf16 tokens in virtual pages of 64
+    jb = max(0, itm.y);
+    nb = min(bf16_token_count(N, p.n_sink, p.n_recent), jb + max(0, itm.z));
+    n_blocks = nb > jb ? (nb - jb + kPageTokens - 1) / kPageTokens : 0;
   } else {
     page0 = itm.y;
     n_blocks = min(min(itm.z, first_page + n_pp - page0), p.max_pages - page0);
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       // bf16 tokens in virtual pages of 64, the pair's rows 16 pr .. 16 pr + 15 of each
       load_queries();
       for (int t = 0; t < n_blocks; ++t) {
-        const int j = t * kPageTokens + row;
+        const int j = jb + t * kPageTokens + row;
         const bool valid = j < nb;
         const uint16_t* src = nullptr;  // masked lanes read nothing
         if (valid) {

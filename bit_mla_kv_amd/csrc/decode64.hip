@@ -180,12 +180,15 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   const int p_lo = p.n_sink, p_hi = N - p.n_recent;
   const int first_page = p_lo / kPageTokens;
   const int n_pp = p_hi > p_lo ? (p_hi - 1) / kPageTokens - first_page + 1 : 0;
-  int n_tiles, page0 = 0, ns = 0, nb = 0, rstart = 0;
+  // a bf16 item holds entries [jb, nb) of the sequence's bf16 token list (sink tokens, then the
+  // recent window from rstart on)
+  int n_tiles, page0 = 0, ns = 0, nb = 0, rstart = 0, jb = 0;
   if (!packed) {
     ns = min(p.n_sink, N);
     rstart = max(p.n_sink, N - p.n_recent);
-    nb = ns + max(0, N - rstart);
-    n_tiles = (nb + kT - 1) / kT;
+    jb = max(0, itm.y);
+    nb = min(bf16_token_count(N, p.n_sink, p.n_recent), jb + max(0, itm.z));
+    n_tiles = nb > jb ? (nb - jb + kT - 1) / kT : 0;
   } else {
     page0 = itm.y;
     n_tiles = 2 * min(itm.z, first_page + n_pp - page0);
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       if (!packed) {
         for (int e = ft; e < kT * (kD / 8); e += 256) {
           const int r = e / (kD / 8), m = e % (kD / 8);
-          const int j = t * kT + r;
+          const int j = jb + t * kT + r;
           uint4 o = make_uint4(0, 0, 0, 0);
           if (j < nb) {
             const uint16_t* src;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         }
         if (ft < kT) {
           const int r = ft;
-          const bool valid = t * kT + r < nb;
+          const bool valid = jb + t * kT + r < nb;
 #pragma unroll
           for (int g = 0; g < kGroups; ++g) sm.sq[sl][g][sq_pos(r)] = valid ? c_log2 : 0.f;
 #pragma unroll

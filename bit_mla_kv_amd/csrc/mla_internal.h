@@ -17,6 +17,14 @@ __host__ __device__ inline int page_bytes(int bits_c) {
   return kPageTokens * (content_row_bytes(bits_c) + kDr / 2 + 4 * kGroups);
 }
 
+// Number of a sequence's tokens read from bf16: the first min(n_sink, N), then the recent window
+// [max(n_sink, N - n_recent), N); each token once.
+__host__ __device__ inline int bf16_token_count(int N, int n_sink, int n_recent) {
+  const int ns = N < n_sink ? N : n_sink;
+  const int rstart = n_sink > N - n_recent ? n_sink : N - n_recent;
+  return ns + (N - rstart > 0 ? N - rstart : 0);
+}
+
 struct AppendParams {
   uint8_t* pages;
   int64_t num_pages;

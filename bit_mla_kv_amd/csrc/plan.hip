@@ -2,10 +2,11 @@
 //
 // plan_kernel (one workgroup) turns the device-resident sequence lengths into
 // a balanced work list: every sequence's packed range [n_sink, N - n_recent)
-// is cut into page-aligned chunks of one common size P = ceil(total packed
-// pages / target items), and every sequence gets one more item for its bf16
-// (sink + recent) tokens.  Items are ordered full chunks first, then the
-// shorter tail chunks, then the bf16 items, so the hardware's in-order
+// is cut into page-aligned chunks of one common size P = ceil(total pages /
+// target items), and its list of bf16 (sink + recent) tokens into chunks of
+// 64 P tokens (one item when, as usual, there are at most 132; many when the
+// recent window is long).  Items are ordered full chunks first, then the
+// shorter tail chunks, then the bf16 chunks, so the hardware's in-order
 // dispatch starts the longest work first.  When a slightly longer chunk lets
 // every item run at once (one round of workgroups), that chunk is used.  combine_kernel merges each
 // sequence's partial results exactly (max-shifted sums), adding the deferred
@@ -29,6 +30,19 @@ __device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, in
   *first_page = p_lo / kPageTokens;
   return p_hi > p_lo ? (p_hi - 1) / kPageTokens - *first_page + 1 : 0;
 }
+// the sequence's bf16 tokens (sink, then the recent window) and their count in 64-token pages
+__device__ __forceinline__ int seq_bf16_tokens(const DecodeParams& p, int b) {
+  int N = p.seq_len[b];
+  const int slot = p.seq_slot[b];
+  if (slot < 0 || slot >= p.num_slots) N = 0;
+  return bf16_token_count(N, p.n_sink, p.n_recent);
+}
+__device__ __forceinline__ int seq_bf16_pages(const DecodeParams& p, int b) {
+  return (seq_bf16_tokens(p, b) + kPageTokens - 1) / kPageTokens;
+}
+// bf16 items of a sequence with chunks of pps pages: at least one (an empty sequence still leaves
+// a partial row for the combine)
+__device__ __forceinline__ int bf16_items(int bf_pages, int pps) { return max(1, (bf_pages + pps - 1) / pps); }
 
 // exclusive scan over the 64 lanes of the wave; *total gets the sum
 __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
@@ -49,7 +63,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   long long local = 0;
   for (int b = t; b < p.batch; b += kPlanThreads) {
     int fp;
-    local += seq_packed_pages(p, b, &fp);
+    local += seq_packed_pages(p, b, &fp) + seq_bf16_pages(p, b);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
@@ -60,24 +74,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   // by up to 2 x batch, and the excess then runs as a second round after a full chunk.  When a
   // chunk at most a quarter longer brings every item into one round, take the shortest such chunk.
   if (p.batch <= kPlanThreads * kPlanRegs && 2 * p.batch <= p.target_items) {
-    int n_reg[kPlanRegs];
+    int n_reg[kPlanRegs], f_reg[kPlanRegs];
     int n_max = 0;
 #pragma unroll
     for (int k = 0; k < kPlanRegs; ++k) {
       const int b = t + kPlanThreads * k;
       int fp;
       n_reg[k] = b < p.batch ? seq_packed_pages(p, b, &fp) : 0;
-      n_max = std::max(n_max, n_reg[k]);
+      f_reg[k] = b < p.batch ? seq_bf16_pages(p, b) : -1;  // -1: no sequence, no bf16 item
+      n_max = std::max(n_max, std::max(n_reg[k], f_reg[k]));
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
     auto items_at = [&](int c) {  // all items of a plan with chunks of c pages
       int n = 0;
 #pragma unroll
-      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c;
+      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c + (f_reg[k] >= 0 ? bf16_items(f_reg[k], c) : 0);
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
-      return n + p.batch;
+      return n;
     };
     int lo = pps, hi = std::min(std::max(n_max, pps), pps + pps / 4);
     if (items_at(lo) > p.target_items && items_at(hi) <= p.target_items) {
@@ -91,36 +106,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   }
   if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
 
-  // pass 1: counts of full / tail items, scanned in chunks of 64 sequences (lane t owns sequence
-  // b0 + t in both passes, so it reads back only what it wrote itself)
-  int full_base = 0, tail_base = 0;
+  // pass 1: counts of full / tail / bf16 items, scanned in chunks of 64 sequences (lane t owns
+  // sequence b0 + t in both passes, so it reads back only what it wrote itself)
+  int full_base = 0, tail_base = 0, bf_base = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kPlanThreads) {
     const int b = b0 + t;
-    int nf = 0, nt = 0, fp = 0;
+    int nf = 0, nt = 0, nbi = 0, fp = 0;
     if (b < p.batch) {
       const int n = seq_packed_pages(p, b, &fp);
       nf = n / pps;
       nt = (n % pps) != 0;
+      nbi = bf16_items(seq_bf16_pages(p, b), pps);
     }
-    int tf, tt;
+    int tf, tt, tb;
     const int of = wave_exclusive_scan(nf, &tf);
     const int ot = wave_exclusive_scan(nt, &tt);
+    const int ob = wave_exclusive_scan(nbi, &tb);
     if (b < p.batch) {
       p.seq_info[4 * b + 0] = full_base + of;  // first full item
       p.seq_info[4 * b + 1] = nf;
       p.seq_info[4 * b + 2] = nt ? tail_base + ot : -1;
-      p.seq_info[4 * b + 3] = fp;              // first packed page (temporarily)
+      p.seq_info[4 * b + 3] = bf_base + ob;    // first bf16 item, relative (temporarily)
     }
     full_base += tf;
     tail_base += tt;
+    bf_base += tb;
   }
-  const int F = full_base, T = tail_base;
+  const int F = full_base, T = tail_base, BF = bf_base;
   // pass 2: emit items (b, first page, pages, kind)
   for (int b = t; b < p.batch; b += kPlanThreads) {
     const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1], tl = p.seq_info[4 * b + 2];
-    const int fp = p.seq_info[4 * b + 3];
-    int fp2;
-    const int n = seq_packed_pages(p, b, &fp2);
+    const int bo = F + T + p.seq_info[4 * b + 3];
+    int fp;
+    const int n = seq_packed_pages(p, b, &fp);
     // capacity guards only matter when a caller breaks the seq_len <= max_seq_len contract
     for (int k = 0; k < nf && fo + k < p.max_items; ++k)
       reinterpret_cast<int4*>(p.items)[fo + k] = make_int4(b, fp + k * pps, pps, 0);
@@ -128,12 +146,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
       if (F + tl < p.max_items) reinterpret_cast<int4*>(p.items)[F + tl] = make_int4(b, fp + nf * pps, n - nf * pps, 0);
       p.seq_info[4 * b + 2] = F + tl < p.max_items ? F + tl : -1;
     }
-    if (F + T + b < p.max_items) reinterpret_cast<int4*>(p.items)[F + T + b] = make_int4(b, 0, 0, 1);
-    p.seq_info[4 * b + 3] = F + T + b < p.max_items ? F + T + b : -1;  // bf16 item
+    // bf16 chunks (first index into the sequence's bf16 token list, count)
+    const int nbt = seq_bf16_tokens(p, b), chunk = pps * kPageTokens;
+    const int nbi = bf16_items(seq_bf16_pages(p, b), pps);
+    for (int k = 0; k < nbi && bo + k < p.max_items; ++k)
+      reinterpret_cast<int4*>(p.items)[bo + k] = make_int4(b, k * chunk, min(chunk, nbt - k * chunk), 1);
+    p.seq_info[4 * b + 3] = bo < p.max_items ? bo : -1;  // first bf16 item
     if (fo + nf > p.max_items) p.seq_info[4 * b + 1] = max(0, p.max_items - fo);
   }
   if (t == 0) {
-    p.plan_hdr[0] = F + T + p.batch;  // item count
+    p.plan_hdr[0] = F + T + BF;  // item count
     p.plan_hdr[1] = pps;
   }
 }
@@ -159,8 +181,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
   const int w = threadIdx.x >> 6;
   const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
   const int tl = p.seq_info[4 * b + 2], bi = p.seq_info[4 * b + 3];
-  const int n_rows = nf + (tl >= 0) + (bi >= 0);
-  auto item_of = [&](int k) { return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi); };
+  // the sequence's bf16 chunks are consecutive items from bi on (chunks of 64 P tokens)
+  const int nbi = bi < 0 ? 0 : min(bf16_items(seq_bf16_pages(p, b), p.plan_hdr[1]), min(p.plan_hdr[0], p.max_items) - bi);
+  const int n_rows = nf + (tl >= 0) + nbi;
+  auto item_of = [&](int k) {
+    return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi + (k - nf - (tl >= 0)));
+  };
   // lane's channels: 4 lane .. 4 lane + 3 (group lane / 16) and 256 + 4 lane .. (group 4 + lane / 16)
   const int g0 = lane / 16, g1 = 4 + lane / 16;
 

@@ -197,6 +197,30 @@ def test_all_bf16_mode():
     check(out, lse, ro, rl, "all-bf16")
 
 
+@pytest.mark.parametrize("heads", [16, 64])
+def test_all_bf16_long_window_chunks(heads):
+    """A long recent window (n_recent >= N): the bf16 token lists are split over many items
+    (chunks of 64 P tokens, P pages per split), merged exactly by the combine; the output must not
+    depend on the chunking."""
+    lens = [3000, 700, 1, 0]
+    rows = [mi.rows(46, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(46, len(lens), heads)
+    cache = build(rows, 4, seed=46, n_recent=4096)
+    ro, rl = reference(rows, q, 4, SCALE, n_recent=4096)
+    outs = []
+    for pps in ("1", "3", None):
+        if pps is not None:
+            os.environ["MLA_LOWBIT_PAGES_PER_SPLIT"] = pps
+        try:
+            out, lse = run_decode(cache, q, lens)
+        finally:
+            os.environ.pop("MLA_LOWBIT_PAGES_PER_SPLIT", None)
+        check(out, lse, ro, rl, f"all-bf16 H{heads} pps={pps}")
+        outs.append(bf16_tensor_to_f64(out))
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 4e-3 * np.max(np.abs(outs[0]))
+
+
 def test_exactly_once_canaries():
     """NaN in every representation a token must NOT be read from leaves the output unchanged."""
     lens = [1000, 150, 2, 0]
