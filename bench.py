@@ -12,6 +12,12 @@ per launch / its own duration from HIP events on its stream) and the CPU
 oracle's throughput on a bounded sample.
 
     python bench.py [--workload dsv3_c4r4_128k] [--steps 50] [--warmup 10]
+
+With --bf16-sweep it instead times the decode call (plan + decode + combine)
+of the same kernels on a C4R4 cache and on an all-bf16 cache (recent window
+>= N, so every token is read from bf16) at the workload's head count, for
+contexts 1K..1M at batch 8 and 32, the comparison the pages make between the
+low-bit and the bf16 cache; one JSON line with every point.
 """
 from __future__ import annotations
 
@@ -45,6 +51,10 @@ def parse():
                     help="cache copies rotated across steps so the 256 MB Infinity Cache cannot serve them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--bf16-sweep", action="store_true",
+                    help="C4R4 vs all-bf16 decode latency at contexts 1K..1M, batch 8 and 32")
+    ap.add_argument("--sweep-contexts", default="1024,4096,16384,65536,131072,1048576")
+    ap.add_argument("--sweep-batches", default="8,32")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -144,12 +154,83 @@ def committed_traffic(workload):
     return float(m_val.group(1))
 
 
+def bf16_sweep(args):
+    """Decode latency of a C4R4 cache vs an all-bf16 cache (n_recent >= N) on the same kernels.
+    Every sequence holds the same synthetic rows (the timing does not depend on the values); both
+    caches are filled through the HIP writer from one device copy of the rows."""
+    import torch
+    import mla_inputs as mi
+    import bit_mla_kv_amd as m
+    from bit_mla_kv_amd import cache_builder as cb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = mi.workload(args.workload)
+    H = w.heads
+    contexts = [int(x) for x in args.sweep_contexts.split(",")]
+    batches = [int(x) for x in args.sweep_batches.split(",")]
+    n_max = max(contexts)
+    rows = cb.to_device_bf16(mi.rows(w.seed, 0, n_max, mi.outlier_channels(w.seed), threads=16), dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hip = Hip()
+    steps, warm = max(3, min(args.steps, 20)), max(1, min(args.warmup, 5))
+
+    def fill(layout, B, N):
+        cache = cb.allocate_for(layout, [N] * B, mi.page_permutation(w.seed, B * ((N + 63) // 64) + 8), device=dev)
+        lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+        for b in range(B):
+            for c0 in range(0, N, 1 << 20):
+                c1 = min(N, c0 + (1 << 20))
+                m.quantize_append(cache, rows[c0:c1], torch.full((c1 - c0,), b, dtype=torch.int32, device=dev),
+                                  torch.arange(c0, c1, dtype=torch.int32, device=dev), lens, stream=sh)
+        return cache
+
+    def time_decode(cache, B, N):
+        q = cb.to_device_bf16(mi.queries(w.seed, B, H).reshape(B * H, -1), dev).view(B, H, 576)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        ws = m.alloc_workspace(cache.layout, B, H, N, dev)
+        slots = torch.arange(B, dtype=torch.int32, device=dev)
+        lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+        for _ in range(warm):
+            m.decode(cache, q, slots, lens, N, w.scale, out, lse, ws, stream=sh)
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sh)
+        for _ in range(steps):
+            m.decode(cache, q, slots, lens, N, w.scale, out, lse, ws, stream=sh)
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(e0, e1) / steps
+
+    points = []
+    for B in batches:
+        for N in contexts:
+            res = {"batch": B, "context": N}
+            for mode, layout in (("c4r4", m.make_layout(w.bits_c)), ("bf16", m.make_layout(w.bits_c, 4, max(N, 128)))):
+                cache = fill(layout, B, N)
+                torch.cuda.synchronize()
+                res[f"{mode}_ms"] = round(time_decode(cache, B, N), 5)
+                del cache
+                torch.cuda.empty_cache()
+            res["c4r4_vs_bf16_pct"] = round(100.0 * (res["c4r4_ms"] / res["bf16_ms"] - 1.0), 2)
+            print(json.dumps(res), file=sys.stderr, flush=True)
+            points.append(res)
+    print(json.dumps({"metric": "decode latency, C4R4 cache vs all-bf16 cache on the same kernels",
+                      "unit": "ms per decode call (plan + decode + combine)", "n_gpus": 1, "heads": H,
+                      "bits": f"C{w.bits_c}R4", "steps": steps, "warmup": warm, "data": "synthetic",
+                      "points": points}))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the low-bit MLA decode path is built and timed on a single "
               "MI355X (run without --gpus or with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.bf16_sweep:
+        bf16_sweep(args)
+        return
 
     import torch
     import mla_inputs as mi

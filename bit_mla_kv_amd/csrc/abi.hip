@@ -35,8 +35,8 @@ int check_layout(const mla_lowbit_layout* L) {
   if ((L->bits_c != 4 && L->bits_c != 2) || L->bits_r != 4)
     return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "bits (c=%d, r=%d) unsupported; need c in {4,2}, r = 4", L->bits_c,
                 L->bits_r);
-  if (L->n_sink < 0 || L->n_sink > 64 || L->n_recent < 1 || L->n_recent > 8192)
-    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "n_sink=%d / n_recent=%d outside [0,64] / [1,8192]", L->n_sink,
+  if (L->n_sink < 0 || L->n_sink > 64 || L->n_recent < 1 || L->n_recent > (1 << 24))
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "n_sink=%d / n_recent=%d outside [0,64] / [1,2^24]", L->n_sink,
                 L->n_recent);
   return MLA_LOWBIT_OK;
 }

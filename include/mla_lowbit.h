@@ -45,8 +45,9 @@
  *    must have |x| < 65504 (finite); NaN/Inf inputs are out of contract.
  *
  * Supported layout: d_c = 512, d_r = 64, group = 64, page_tokens = 64,
- * bits_c in {4, 2}, bits_r = 4, 0 <= n_sink <= 64, 1 <= n_recent <= 8192
- * (n_recent >= every sequence length gives an all-bf16 cache).  num_heads
+ * bits_c in {4, 2}, bits_r = 4, 0 <= n_sink <= 64, 1 <= n_recent <= 2^24
+ * (n_recent >= every sequence length gives an all-bf16 cache; long bf16
+ * token lists are split over several work items like the packed pages).  num_heads
  * must be a positive multiple of 16.  Anything else returns
  * MLA_LOWBIT_ERR_UNSUPPORTED.
  */

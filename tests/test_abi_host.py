@@ -66,6 +66,10 @@ def test_append_validation(m):
     c4.layout.n_recent = 0
     assert A(ctypes.byref(c4), 0x1000, 0x1000, 0x1000, 0x1000, 4, None) == m.ERR_UNSUPPORTED
     assert "n_recent" in L.mla_lowbit_last_error().decode()
+    c4.layout.n_recent = (1 << 24) + 1
+    assert A(ctypes.byref(c4), 0x1000, 0x1000, 0x1000, 0x1000, 4, None) == m.ERR_UNSUPPORTED
+    c4.layout.n_recent = 1 << 20  # a long all-bf16 window is a supported layout
+    assert m.page_bytes(c4.layout) == 20736
 
 
 def test_decode_validation(m):
