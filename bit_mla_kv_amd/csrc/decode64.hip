@@ -31,6 +31,7 @@
 // Partials are left unnormalised with their running max and sum; the combine
 // kernel adds the zero terms and merges splits.
 #include <algorithm>
+#include <type_traits>
 
 #include "decode_common.h"
 
@@ -204,6 +205,40 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   const float c_log2 = p.scale_log2e;
   const int64_t row0 = (int64_t)item * p.heads + head0;  // first workspace row of this workgroup
 
+  // bf16 items: the 16-byte chunks of a tile's rows (32 tokens x 72 chunks) are spread over all
+  // 512 threads (chunk tid + 512 e; the fifth, e = 4, exists only for the QK threads), requested at
+  // the start of a step and converted into the tile at its end, so their latency hides behind the
+  // step's QK / PV work
+  constexpr int kBfChunks = kT * (kD / 8);
+  static_assert(kBfChunks == 4 * kThreads + 256, "chunk split assumes 2304 chunks a tile");
+  constexpr int kBfQK = 5, kBfPV = 4;
+  struct BfRegs {
+    uint4 x[kBfQK];
+  };
+  auto bf_load = [&](int t, BfRegs& R, auto per) {
+#pragma unroll
+    for (int e = 0; e < decltype(per)::value; ++e) {
+      const int u = tid + kThreads * e, r = u / (kD / 8), m = u % (kD / 8);
+      const int j = jb + t * kT + r;
+      R.x[e] = make_uint4(0, 0, 0, 0);
+      if (u < kBfChunks && j < nb) {
+        const uint16_t* src = j < ns ? p.sink + ((int64_t)slot * p.n_sink + j) * kD
+                                     : p.recent + ((int64_t)slot * p.n_recent + (rstart + (j - ns)) % p.n_recent) * kD;
+        R.x[e] = *reinterpret_cast<const uint4*>(src + 8 * m);
+      }
+    }
+  };
+  auto bf_store = [&](int t, const BfRegs& R, auto per) {
+    f16* tile = &sm.tile[t % kSlots][0];
+#pragma unroll
+    for (int e = 0; e < decltype(per)::value; ++e) {
+      const int u = tid + kThreads * e, r = u / (kD / 8), m = u % (kD / 8);
+      if (u < kBfChunks)
+        *reinterpret_cast<uint4*>(&tile[r * kS + 8 * m]) =
+            m < kDc / 8 ? bf16_chunk_to_f16<BITS_C>(R.x[e]) : bf16_chunk_to_f16<4>(R.x[e]);
+    }
+  };
+
   if (w < 4) {
     // ====== QK + unpack waves: QK of heads head0 + 16w + L16, unpacking of a quarter of each tile ======
     const int ft = tid;  // 0 .. 255
@@ -227,24 +262,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     auto fill = [&](int t, const TileRegs<BITS_C>& R) {
       const int sl = t % kSlots;
       f16* tile = &sm.tile[sl][0];
-      if (!packed) {
-        for (int e = ft; e < kT * (kD / 8); e += 256) {
-          const int r = e / (kD / 8), m = e % (kD / 8);
-          const int j = jb + t * kT + r;
-          uint4 o = make_uint4(0, 0, 0, 0);
-          if (j < nb) {
-            const uint16_t* src;
-            if (j < ns) {
-              src = p.sink + ((int64_t)slot * p.n_sink + j) * kD;
-            } else {
-              const int tt = rstart + (j - ns);
-              src = p.recent + ((int64_t)slot * p.n_recent + tt % p.n_recent) * kD;
-            }
-            const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * m);
-            o = m < kDc / 8 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw);
-          }
-          *reinterpret_cast<uint4*>(&tile[r * kS + 8 * m]) = o;
-        }
+      if (!packed) {  // the rows themselves come through bf_load / bf_store
         if (ft < kT) {
           const int r = ft;
           const bool valid = jb + t * kT + r < nb;
@@ -433,12 +451,22 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
     } else {
       const TileRegs<BITS_C> none{};
+      BfRegs X;
       load_queries();
-      if (n_tiles > 0) fill(0, none);
-      __syncthreads();  // first tile unpacked
+      if (n_tiles > 0) {
+        bf_load(0, X, std::integral_constant<int, kBfQK>{});
+        bf_store(0, X, std::integral_constant<int, kBfQK>{});
+        fill(0, none);
+      }
+      __syncthreads();  // first tile converted
       for (int k = 0; k < n_steps; ++k) {
+        const bool next = k + 1 < n_tiles;
+        if (next) bf_load(k + 1, X, std::integral_constant<int, kBfQK>{});
         qk_step(k);
-        if (k + 1 < n_tiles) fill(k + 1, none);
+        if (next) {
+          bf_store(k + 1, X, std::integral_constant<int, kBfQK>{});
+          fill(k + 1, none);
+        }
         __syncthreads();
       }
     }
@@ -550,9 +578,17 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
     } else {
-      __syncthreads();  // first tile unpacked
+      BfRegs X;
+      if (n_tiles > 0) {
+        bf_load(0, X, std::integral_constant<int, kBfPV>{});
+        bf_store(0, X, std::integral_constant<int, kBfPV>{});
+      }
+      __syncthreads();  // first tile converted
       for (int k = 0; k < n_steps; ++k) {
+        const bool next = k + 1 < n_tiles;
+        if (next) bf_load(k + 1, X, std::integral_constant<int, kBfPV>{});
         pv_step(k);
+        if (next) bf_store(k + 1, X, std::integral_constant<int, kBfPV>{});
         __syncthreads();
       }
     }
