@@ -177,14 +177,23 @@ def bf16_sweep(args):
     steps, warm = max(3, min(args.steps, 20)), max(1, min(args.warmup, 5))
 
     def fill(layout, B, N):
+        """Prefill every slot through the writer in chunks of up to 1M tokens a call; returns the
+        cache and the writer's GPU time (HIP events around its calls only)."""
         cache = cb.allocate_for(layout, [N] * B, mi.page_permutation(w.seed, B * ((N + 63) // 64) + 8), device=dev)
         lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+        calls = []
         for b in range(B):
             for c0 in range(0, N, 1 << 20):
                 c1 = min(N, c0 + (1 << 20))
-                m.quantize_append(cache, rows[c0:c1], torch.full((c1 - c0,), b, dtype=torch.int32, device=dev),
-                                  torch.arange(c0, c1, dtype=torch.int32, device=dev), lens, stream=sh)
-        return cache
+                calls.append((torch.full((c1 - c0,), b, dtype=torch.int32, device=dev),
+                              torch.arange(c0, c1, dtype=torch.int32, device=dev), c0, c1))
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sh)
+        for sl, pos, c0, c1 in calls:
+            m.quantize_append(cache, rows[c0:c1], sl, pos, lens, stream=sh)
+        hip.record(e1, sh)
+        return cache, hip.elapsed_ms(e0, e1)
 
     def time_decode(cache, B, N):
         q = cb.to_device_bf16(mi.queries(w.seed, B, H).reshape(B * H, -1), dev).view(B, H, 576)
@@ -208,8 +217,10 @@ def bf16_sweep(args):
         for N in contexts:
             res = {"batch": B, "context": N}
             for mode, layout in (("c4r4", m.make_layout(w.bits_c)), ("bf16", m.make_layout(w.bits_c, 4, max(N, 128)))):
-                cache = fill(layout, B, N)
+                cache, t_fill = fill(layout, B, N)
                 torch.cuda.synchronize()
+                if mode == "c4r4":  # prefill of B x N tokens (quantize, pack, sink / ring copies)
+                    res["prefill_tokens_per_s"] = round(B * N / (t_fill * 1e-3), 1)
                 res[f"{mode}_ms"] = round(time_decode(cache, B, N), 5)
                 del cache
                 torch.cuda.empty_cache()

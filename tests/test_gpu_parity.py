@@ -133,6 +133,48 @@ def test_writer_stream_equals_bulk():
     check_bf16_buffers(stream, [rows])
 
 
+def _append(cache, rows_by_slot, items, lens_after):
+    """One quantize_append call: items = [(slot, pos)], rows taken from rows_by_slot[slot][pos]."""
+    dev = cache.pages.device
+    kv = np.stack([rows_by_slot[s][p] for s, p in items])
+    m.quantize_append(cache, cb.to_device_bf16(kv, dev),
+                      torch.tensor([s for s, _ in items], dtype=torch.int32, device=dev),
+                      torch.tensor([p for _, p in items], dtype=torch.int32, device=dev),
+                      torch.tensor(lens_after, dtype=torch.int32, device=dev))
+
+
+@pytest.mark.parametrize("bits_c", [4, 2])
+def test_writer_chunked_prefill_and_rebuild(bits_c):
+    """Chunked prefill with several slots' tokens interleaved in one call, then a preempted slot
+    rebuilt from position 0 on other pages (recompute) while other slots keep appending: the final
+    pages, sink and ring rows are bit-exact with the oracle's bulk quantization."""
+    rng = np.random.default_rng(24)
+    lens = [500, 300, 140, 300]  # slot 3 only lends its pages to slot 1's rebuild
+    rows = [mi.rows(24, b, n) for b, n in enumerate(lens)]
+    stale = mi.rows(25, 1, 200)  # slot 1's content before it is preempted
+    layout = m.make_layout(bits_c)
+    cache = cb.allocate_for(layout, lens, mi.page_permutation(24, sum((n + 63) // 64 for n in lens) + 3))
+    first = [(0, p) for p in range(300)] + [(1, p) for p in range(200)] + [(2, p) for p in range(140)]
+    first = [first[i] for i in rng.permutation(len(first))]
+    _append(cache, [rows[0], stale, rows[2], None], first, [300, 200, 140, 0])
+    # preemption: slot 1 takes slot 3's pages and is recomputed from position 0 in two chunks
+    cache.block_table[1] = cache.block_table[3]
+    second = [(0, p) for p in range(300, 500)] + [(1, p) for p in range(150)]
+    second = [second[i] for i in rng.permutation(len(second))]
+    _append(cache, rows, second, [500, 150, 140, 0])
+    _append(cache, rows, [(1, p) for p in range(150, 300)], [500, 300, 140, 0])
+    torch.cuda.synchronize()
+    pool = cache.pages.cpu().numpy()
+    bt = cache.block_table.cpu().numpy()
+    for b in (0, 1, 2):
+        cc, cr, meta = oracle.quantize(rows[b], bits_c)
+        exp = np.zeros_like(pool)
+        oracle.place_pages(exp, bt[b], cc, cr, meta, bits_c)
+        used = bt[b][: (lens[b] + 63) // 64]
+        assert np.array_equal(pool[used], exp[used]), f"slot {b}"
+    check_bf16_buffers(cache, rows[:3] + [np.zeros((0, 576), np.uint16)])
+
+
 # ------------------------------------------------------------------- decode
 def test_decode_tiny_c4r4():
     """The tiny workload: batch 1, 16 heads, 1024 tokens."""
