@@ -17,7 +17,9 @@ With --bf16-sweep it instead times the decode call (plan + decode + combine)
 of the same kernels on a C4R4 cache and on an all-bf16 cache (recent window
 >= N, so every token is read from bf16) at the workload's head count, for
 contexts 1K..1M at batch 8 and 32, the comparison the pages make between the
-low-bit and the bf16 cache; one JSON line with every point.
+low-bit and the bf16 cache; one JSON line with every point.  With --mtp it
+times the decode of 1, 2 and 4 query tokens per sequence (speculative steps,
+causal visibility) on the workload's cache: the queries share one read of it.
 """
 from __future__ import annotations
 
@@ -53,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--bf16-sweep", action="store_true",
                     help="C4R4 vs all-bf16 decode latency at contexts 1K..1M, batch 8 and 32")
+    ap.add_argument("--mtp", action="store_true",
+                    help="decode of 1, 2 and 4 query tokens per sequence on the workload's cache")
     ap.add_argument("--sweep-contexts", default="1024,4096,16384,65536,131072,1048576")
     ap.add_argument("--sweep-batches", default="8,32")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -233,6 +237,53 @@ def bf16_sweep(args):
                       "points": points}))
 
 
+def mtp(args):
+    """Decode of q_len = 1, 2, 4 query tokens per sequence on one cache of the workload's shape."""
+    import torch
+    import mla_inputs as mi
+    import bit_mla_kv_amd as m
+    from bit_mla_kv_amd import cache_builder as cb
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = mi.workload(args.workload)
+    B, H = w.batch, w.heads
+    lens = w.seq_lens.astype(np.int64)
+    layout = m.make_layout(w.bits_c)
+    cache = cb.allocate_for(layout, lens, mi.page_permutation(w.seed, int(((lens + 63) // 64).sum()) + 8), device=dev)
+    outl = mi.outlier_channels(w.seed)
+    for b in range(B):
+        cb.prefill(cache, b, mi.rows(w.seed, b, int(lens[b]), outl, threads=16))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hip = Hip()
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    max_len = int(lens.max())
+    steps, warm = max(3, min(args.steps, 30)), max(1, min(args.warmup, 5))
+    points = []
+    for q_len in (1, 2, 4):
+        q = cb.to_device_bf16(mi.queries(w.seed, B * q_len, H).reshape(B * q_len * H, -1), dev).view(B, q_len, H, 576)
+        out = torch.empty((B, q_len, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=dev)
+        ws = m.alloc_workspace(layout, B, q_len * H, max_len, dev)
+        for _ in range(warm):
+            m.decode_multi(cache, q, slots, sl, max_len, w.scale, out, lse, ws, stream=sh)
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sh)
+        for _ in range(steps):
+            m.decode_multi(cache, q, slots, sl, max_len, w.scale, out, lse, ws, stream=sh)
+        hip.record(e1, sh)
+        ms = hip.elapsed_ms(e0, e1) / steps
+        points.append({"q_len": q_len, "ms": round(ms, 5), "ms_per_query": round(ms / q_len, 5),
+                       "kv_tokens_per_s": round(float(lens.sum()) / (ms * 1e-3), 1)})
+    print(json.dumps({"metric": "multi-token query decode (plan + decode + combine) on one cache",
+                      "unit": "ms per decode call", "n_gpus": 1, "workload": w.name, "batch": B, "heads": H,
+                      "context": int(max_len), "steps": steps, "warmup": warm, "data": "synthetic",
+                      "points": points}))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -241,6 +292,9 @@ def main():
         sys.exit(2)
     if args.bf16_sweep:
         bf16_sweep(args)
+        return
+    if args.mtp:
+        mtp(args)
         return
 
     import torch

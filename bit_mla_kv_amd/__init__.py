@@ -53,6 +53,9 @@ def _load():
     L.mla_lowbit_decode_workspace_bytes.restype = SZ
     L.mla_lowbit_decode.argtypes = [ctypes.POINTER(CacheDesc), P, P, P, I32, I32, I32, ctypes.c_float, P, P, P, SZ, P]
     L.mla_lowbit_decode.restype = ctypes.c_int
+    L.mla_lowbit_decode_multi.argtypes = [ctypes.POINTER(CacheDesc), P, P, P, I32, I32, I32, I32, ctypes.c_float,
+                                          P, P, P, SZ, P]
+    L.mla_lowbit_decode_multi.restype = ctypes.c_int
     L.mla_lowbit_status_string.argtypes = [ctypes.c_int]
     L.mla_lowbit_status_string.restype = ctypes.c_char_p
     L.mla_lowbit_profile_decode_events.argtypes = [P, P]
@@ -64,7 +67,7 @@ def _load():
 
 lib = _load()
 EXPORTS = ("mla_lowbit_page_bytes", "mla_lowbit_quantize_append", "mla_lowbit_decode_workspace_bytes",
-           "mla_lowbit_decode", "mla_lowbit_profile_decode_events", "mla_lowbit_status_string",
+           "mla_lowbit_decode", "mla_lowbit_decode_multi", "mla_lowbit_profile_decode_events", "mla_lowbit_status_string",
            "mla_lowbit_last_error")
 
 
@@ -148,6 +151,18 @@ def decode(cache: PagedCache, q: torch.Tensor, seq_slot: torch.Tensor, seq_len: 
     _check(lib.mla_lowbit_decode(ctypes.byref(d), _ptr(q), _ptr(seq_slot), _ptr(seq_len), batch, heads,
                                  max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_multi(cache: PagedCache, q: torch.Tensor, seq_slot: torch.Tensor, seq_len: torch.Tensor,
+                 max_seq_len: int, softmax_scale: float, out: torch.Tensor, lse: torch.Tensor | None,
+                 workspace: torch.Tensor, stream=None) -> None:
+    """mla_lowbit_decode_multi: q bf16 [B, q_len, H, 576] -> out bf16 [B, q_len, H, 512], lse fp32
+    [B, q_len, H]; query i of a sequence sees its first seq_len - (q_len - 1 - i) tokens."""
+    batch, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    d = cache.desc
+    _check(lib.mla_lowbit_decode_multi(ctypes.byref(d), _ptr(q), _ptr(seq_slot), _ptr(seq_len), batch, q_len, heads,
+                                       max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def alloc_workspace(layout: Layout, batch: int, heads: int, max_seq_len: int, device="cuda") -> torch.Tensor:

@@ -138,13 +138,20 @@ int mla_lowbit_profile_decode_events(void* start, void* stop) {
 }
 
 static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
-                       int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,
-                       float* lse, void* workspace, size_t workspace_bytes, void* stream, hipEvent_t ev0,
-                       hipEvent_t ev1) {
+                       int32_t batch, int32_t q_len, int32_t heads_per_query, int32_t max_seq_len,
+                       float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream, hipEvent_t ev0, hipEvent_t ev1) {
   int st = check_cache(cache);
   if (st != MLA_LOWBIT_OK) return st;
   if (batch < 0 || max_seq_len < 0)
     return fail(MLA_LOWBIT_ERR_INVALID_ARG, "batch=%d max_seq_len=%d must be >= 0", batch, max_seq_len);
+  if (heads_per_query <= 0 || heads_per_query % 16 != 0)
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "num_heads=%d unsupported (a positive multiple of 16)",
+                heads_per_query);
+  if (q_len < 1 || q_len - 1 > cache->layout.n_recent || (int64_t)q_len * heads_per_query > (1 << 20))
+    return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "q_len=%d unsupported (1 .. n_recent + 1 = %d, q_len * num_heads <= 2^20)",
+                q_len, cache->layout.n_recent + 1);
+  const int32_t num_heads = q_len * heads_per_query;  // rows per sequence
   mla::DecodeConfig cfg;
   if (!mla::decode_config(num_heads, cache->layout.n_sink, cache->layout.n_recent, batch, max_seq_len, &cfg))
     return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "num_heads=%d unsupported (a positive multiple of 16)",
@@ -178,6 +185,8 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.seq_len = seq_len;
   p.batch = batch;
   p.heads = num_heads;
+  p.q_len = q_len;
+  p.heads_per_query = heads_per_query;
   p.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
   p.head_groups = num_heads / cfg.heads_per_wg;
   p.target_items = cfg.target_items;
@@ -209,8 +218,18 @@ int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_
                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
-  return decode_impl(cache, q, seq_slot, seq_len, batch, num_heads, max_seq_len, softmax_scale, out, lse, workspace,
-                     workspace_bytes, stream, ev0, ev1);
+  return decode_impl(cache, q, seq_slot, seq_len, batch, 1, num_heads, max_seq_len, softmax_scale, out, lse,
+                     workspace, workspace_bytes, stream, ev0, ev1);
+}
+
+int mla_lowbit_decode_multi(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot,
+                            const int32_t* seq_len, int32_t batch, int32_t q_len, int32_t num_heads,
+                            int32_t max_seq_len, float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  return decode_impl(cache, q, seq_slot, seq_len, batch, q_len, num_heads, max_seq_len, softmax_scale, out, lse,
+                     workspace, workspace_bytes, stream, ev0, ev1);
 }
 
 }  // extern "C"

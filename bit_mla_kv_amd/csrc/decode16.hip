@@ -420,11 +420,14 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no staging left in flight
     } else {
-      // bf16 tokens in virtual pages of 64, the pair's rows 16 pr .. 16 pr + 15 of each
+      // bf16 tokens in virtual pages of 64, the pair's rows 16 pr .. 16 pr + 15 of each.  With
+      // several query tokens, this workgroup's query sees the first n_vis tokens (the ones it does
+      // not see are all in the recent window, so only bf16 items mask them).
+      const int n_vis = N - (p.q_len - 1 - head0 / p.heads_per_query);
       load_queries();
       for (int t = 0; t < n_blocks; ++t) {
         const int j = jb + t * kPageTokens + row;
-        const bool valid = j < nb;
+        const bool valid = j < nb && (j < ns ? j : rstart + (j - ns)) < n_vis;
         const uint16_t* src = nullptr;  // masked lanes read nothing
         if (valid) {
           if (j < ns) src = p.sink + ((int64_t)slot * p.n_sink + j) * kD;

@@ -392,6 +392,17 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         S[0] = s[0] + mfma16(qz, zr0, z4) + bv[0];
         S[1] = s[1] + mfma16(qz, zr1, z4) + bv[1];
       }
+      if (!packed && p.q_len > 1) {
+        // several query tokens: this wave's query (its 16 heads belong to one) sees the first
+        // n_vis tokens; the ones it does not see are all in the recent window (bf16 items)
+        const int n_vis = N - (p.q_len - 1 - (head0 + 16 * w) / p.heads_per_query);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int j = jb + k * kT + 16 * blk + L16;
+          const int tok = j < ns ? j : rstart + (j - ns);
+          if (tok >= n_vis) S[blk] = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        }
+      }
       // online softmax; a head's running max is refreshed only when one of its scores
       // exceeds it by more than kRescale
       bool need = false;

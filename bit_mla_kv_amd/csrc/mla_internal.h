@@ -54,7 +54,9 @@ struct DecodeParams {
   const uint16_t* q;          // [batch][H][576]
   const int32_t* seq_slot;
   const int32_t* seq_len;
-  int32_t batch, heads;
+  int32_t batch, heads;       // heads: rows per sequence = q_len * heads_per_query
+  int32_t q_len;              // query tokens per sequence; row r is query r / heads_per_query
+  int32_t heads_per_query;    // a multiple of 16, so a 16-row block belongs to one query
   float scale_log2e;          // softmax_scale * log2(e)
   int32_t head_groups;        // heads / heads-per-workgroup
   // split plan (written on the device by plan_kernel)

@@ -169,6 +169,31 @@ int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode of q_len query tokens per sequence at once (speculative / multi-token
+ * prediction steps): every query shares one read of the cache, so the packed
+ * bytes of a page serve q_len * num_heads rows.  Same computation as
+ * mla_lowbit_decode for each query (ai.info summary, "Key Contributions",
+ * item 4), with causal visibility: seq_len counts all q_len new tokens, and
+ * query i (0-based) sees tokens t < seq_len - (q_len - 1 - i), each in the
+ * representation the cache holds for it at length seq_len.
+ *
+ * q           bf16 [batch][q_len][num_heads][d_c+d_r]; 16-byte aligned.
+ * out         bf16 [batch][q_len][num_heads][d_c]; a query that sees no token
+ *             gives zeros.
+ * lse         fp32 [batch][q_len][num_heads] (-inf for no visible token); may be NULL.
+ * workspace   at least mla_lowbit_decode_workspace_bytes(layout, batch,
+ *             q_len * num_heads, max_seq_len) bytes.
+ * Other arguments as mla_lowbit_decode.  1 <= q_len <= n_recent + 1 (the
+ * tokens a query does not see are then in the bf16 recent window), num_heads
+ * a positive multiple of 16, q_len * num_heads <= 2^20; otherwise
+ * MLA_LOWBIT_ERR_UNSUPPORTED.  q_len = 1 is mla_lowbit_decode.
+ */
+int mla_lowbit_decode_multi(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot,
+                            const int32_t* seq_len, int32_t batch, int32_t q_len, int32_t num_heads,
+                            int32_t max_seq_len, float softmax_scale, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid (not needed for decoding).  Arms two caller-created HIP
  * events (hipEvent_t passed as void*) for the NEXT mla_lowbit_decode call on
  * this thread: that call records `start` on its stream immediately before

@@ -105,6 +105,25 @@ def test_decode_validation(m):
     assert call(cache=c2) == m.ERR_UNSUPPORTED
 
 
+def test_decode_multi_validation(m):
+    L = m.lib
+    c = _cache(m)  # n_recent = 128
+    ws = m.decode_workspace_bytes(c.layout, 2, 4 * 16, 4096)
+    assert ws > 0
+
+    def call(q_len, heads=16, wsb=ws):
+        return L.mla_lowbit_decode_multi(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 2, q_len, heads, 4096, 0.07,
+                                         0x4000, 0x5000, 0x100000, wsb, None)
+
+    assert call(0) == m.ERR_UNSUPPORTED
+    assert "q_len" in L.mla_lowbit_last_error().decode()
+    assert call(130) == m.ERR_UNSUPPORTED                 # beyond n_recent + 1
+    assert call(4, heads=8) == m.ERR_UNSUPPORTED          # 32 rows, but 8 heads a query
+    assert call(4, heads=24) == m.ERR_UNSUPPORTED
+    assert call(4, wsb=ws - 1) == m.ERR_WORKSPACE         # the workspace covers q_len * heads rows
+    assert call(129, wsb=0) == m.ERR_WORKSPACE            # n_recent + 1 queries are allowed
+
+
 def test_workspace_monotone(m):
     lay = m.make_layout(4)
     for h in (16, 32, 48, 64, 96, 128, 256):

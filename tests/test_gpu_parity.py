@@ -263,6 +263,64 @@ def test_all_bf16_long_window_chunks(heads):
         assert np.max(np.abs(o - outs[0])) <= 4e-3 * np.max(np.abs(outs[0]))
 
 
+def run_decode_multi(cache, q_u16, lens, max_len=None):
+    """q_u16 [B, q_len, H, 576] -> (out [B, q_len, H, 512], lse [B, q_len, H])."""
+    B, QL, H = q_u16.shape[:3]
+    dev = cache.pages.device
+    max_len = max(max(lens), 1) if max_len is None else max_len
+    q = cb.to_device_bf16(q_u16.reshape(B * QL * H, -1), dev).view(B, QL, H, 576)
+    out = torch.empty((B, QL, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, QL, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(cache.layout, B, QL * H, max_len, dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    m.decode_multi(cache, q, slots, sl, max_len, SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def reference_multi(rows_per_seq, q, bits_c):
+    """Query i of a sequence of N tokens: the oracle's selection at length N (which tokens are
+    bf16 is fixed by the cache), attended over its first N - (q_len - 1 - i) rows."""
+    B, QL, H = q.shape[:3]
+    ro = np.zeros((B, QL, H, 512))
+    rl = np.full((B, QL, H), -np.inf)
+    for b, rows in enumerate(rows_per_seq):
+        n = rows.shape[0]
+        if n == 0:
+            continue
+        cc, cr, meta = oracle.quantize(rows, bits_c)
+        sel = oracle.select(rows, cc, cr, meta, bits_c)
+        for i in range(QL):
+            n_vis = n - (QL - 1 - i)
+            if n_vis > 0:
+                ro[b, i], rl[b, i] = oracle.attend(sel[:n_vis], q[b, i], SCALE)
+    return ro, rl
+
+
+@pytest.mark.parametrize("heads,q_len", [(16, 2), (16, 4), (128, 2), (64, 3)])
+def test_decode_multi_query(heads, q_len):
+    """Several query tokens per sequence with causal visibility; the queries share the cache read
+    (16 heads x 4 queries run as one 64-row group)."""
+    lens = [0, 1, 3, 132, 135, 200, 700, 2049]
+    rows = [mi.rows(47, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(47, len(lens) * q_len, heads).reshape(len(lens), q_len, heads, 576)
+    cache = build(rows, 4, seed=47)
+    out, lse = run_decode_multi(cache, q, lens)
+    ro, rl = reference_multi(rows, q, 4)
+    check(out, lse, ro, rl, f"multi H{heads} q_len {q_len}")
+
+
+def test_decode_multi_single_query_is_decode():
+    lens = [700, 2049]
+    rows = [mi.rows(48, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(48, 2, 16)
+    cache = build(rows, 4, seed=48)
+    o1, l1 = run_decode(cache, q, lens)
+    o2, l2 = run_decode_multi(cache, q.reshape(2, 1, 16, 576), lens)
+    assert torch.equal(o1, o2.view(2, 16, 512)) and torch.equal(l1, l2.view(2, 16))
+
+
 def test_exactly_once_canaries():
     """NaN in every representation a token must NOT be read from leaves the output unchanged."""
     lens = [1000, 150, 2, 0]
