@@ -45,7 +45,7 @@ using namespace dev;
 constexpr int kPairs = 4;             // QK waves 0..3, PV waves 4..7 (pair r: waves r and r + 4)
 constexpr int kThreads = 128 * kPairs;
 constexpr int kB = 16;                // tokens per block (one pair's rows of a page)
-constexpr int kZones = 3;             // staging ring depth per QK wave
+constexpr int kAhead = 3;             // blocks a QK wave holds in registers (block t and two more in flight)
 constexpr int kSV = 528;              // V tile row stride (halves): conflict-free b128 row writes and transposed reads
 constexpr int kPS = 16;               // probability / zero row stride (halves), rows are tokens
 constexpr float kRescale = 8.0f;      // lazy max refresh threshold, log2 units
@@ -57,30 +57,21 @@ struct Geo {
   static constexpr int PB = kPageTokens * (CB + kDr / 2 + 4 * kGroups);   // page bytes
   static constexpr int ROPE0 = kPageTokens * CB;
   static constexpr int META0 = kPageTokens * (CB + kDr / 2);
-  // One block in a staging zone: content rows, RoPE rows, metadata rows.  A content row of CU
-  // 16-byte units sits in RS = CU + 1 slots (the last one left unwritten), so the rows of the 16
-  // tokens start in different LDS banks and a column of units is read without bank conflicts.
-  static constexpr int CU = CB / 16;
-  static constexpr int RS = CU + 1;
-  static constexpr int CI = (kB * RS + 63) / 64;  // content staging instructions (64 slots each)
-  static constexpr int SC = kB * RS * 16;          // RoPE and metadata rows follow the used slots
-  static constexpr int SR = kB * kDr / 2;
-  static constexpr int SM = kB * 4 * kGroups;
-  static constexpr int SZ = SC + SR + SM;
-  static constexpr int LOADS = CI + 2;  // staging instructions per block (content, RoPE, metadata)
-  static_assert(SR <= 1024 && SM <= 1024, "staging split assumes these sizes");
 };
 
-// A pair's tiles: written by its QK wave, read by its PV wave.
+// A pair's tiles for one block: written by its QK wave, read by its PV wave (two buffers a pair:
+// blocks t and t + 1).
 struct __align__(16) PairTiles {
   f16 V[kB][kSV];     // exact content codes of the block [token][channel position]
   f16 P[kB][kPS];     // fp16 probabilities [token][head]
   f16 Z[kB][kPS];     // fp16 zeros [token][z_0..z_7, z_8, 0 x 7]
   f16 SV[8][kB];      // fp16 PV group scales [group][token]
   float alpha[16];    // per-head factor for the PV accumulators before this block (running max refreshed)
+  int resc;           // 1: apply alpha before this block
+  int pad[3];
 };
 union __align__(16) Tiles16 {
-  PairTiles pt[kPairs];
+  PairTiles pt[kPairs][2];
   struct {                   // merge of the pairs' partials at the end (two pairs at a time)
     float o[2][16][kDc];
     float m[kPairs][16], l[kPairs][16];
@@ -124,9 +115,8 @@ __device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
 template <int BITS_C>
 __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   using GE = Geo<BITS_C>;
-  __shared__ __align__(16) uint8_t s_stage[kPairs][kZones][GE::SZ];  // packed blocks, block t in zone t % 3
   __shared__ Tiles16 s_tiles;
-  __shared__ int s_flag[kPairs][4];  // [pair][published block, released block, refresh flag, -]
+  __shared__ int s_flag[kPairs][4];  // [pair][published block, released block, -, -]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,25 +160,26 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   const int last = n_blocks - 1;
 
   if (tid < kPairs * 4) (&s_flag[0][0])[tid] = -1;
-  // LDS addressing: one base pointer per LDS object plus a byte offset.  The compiler ties an
-  // access to its object only through a short chain of address steps, and an access it cannot
-  // tie to an object has to wait for every staging load in flight.
-  const lds_ptr<uint8_t> sb = (lds_ptr<uint8_t>)&s_stage[0][0][0];
+  // LDS addressing: one base pointer per LDS object plus a byte offset (the pair's two buffers
+  // are kPT apart; block t uses buffer t % 2)
   const lds_ptr<uint8_t> tb = (lds_ptr<uint8_t>)&s_tiles;
   lds_vint* const fl = (lds_vint*)&s_flag[pr][0];
   constexpr int kPT = (int)sizeof(PairTiles);
   constexpr int oP = (int)offsetof(PairTiles, P), oZ = (int)offsetof(PairTiles, Z);
   constexpr int oSV = (int)offsetof(PairTiles, SV), oA = (int)offsetof(PairTiles, alpha);
+  constexpr int oR = (int)offsetof(PairTiles, resc);
+  const int pb0 = pr * 2 * kPT;  // the pair's first buffer
   const int rsel = 4 * G + (L16 >> 2), csel = 4 * (L16 & 3);
-  const int o_vtr = pr * kPT + 2 * (rsel * kSV + csel);       // V^T operand, + 32 per 16 channel positions
-  const int o_vwr = pr * kPT + 2 * (L16 * kSV + 16 * G);      // V row slice, + 128 per group
-  const int o_ptr = pr * kPT + oP + 2 * (rsel * kPS + csel);  // P^T operand
-  const int o_pwr = pr * kPT + oP + 2 * (L16 * kPS + 4 * G);
-  const int o_ztr = pr * kPT + oZ + 2 * (rsel * kPS + csel);
-  const int o_zwr = pr * kPT + oZ + 2 * (L16 * kPS);
-  const int o_svr = pr * kPT + oSV + 8 * G;                   // + 32 per group
-  const int o_svw = pr * kPT + oSV + 2 * L16;
-  const int o_al = pr * kPT + oA;
+  const int o_vtr = pb0 + 2 * (rsel * kSV + csel);       // V^T operand, + 32 per 16 channel positions
+  const int o_vwr = pb0 + 2 * (L16 * kSV + 16 * G);      // V row slice, + 128 per group
+  const int o_ptr = pb0 + oP + 2 * (rsel * kPS + csel);  // P^T operand
+  const int o_pwr = pb0 + oP + 2 * (L16 * kPS + 4 * G);
+  const int o_ztr = pb0 + oZ + 2 * (rsel * kPS + csel);
+  const int o_zwr = pb0 + oZ + 2 * (L16 * kPS);
+  const int o_svr = pb0 + oSV + 8 * G;                   // + 32 per group
+  const int o_svw = pb0 + oSV + 2 * L16;
+  const int o_al = pb0 + oA;
+  const int o_rs = pb0 + oR;
   __syncthreads();  // flags initialised
 
   auto& mg = s_tiles.mg;
@@ -231,7 +222,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         qz[j] = (G & 1) ? lo : hi;
       }
     };
-    if (G == 0) *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + 16)) = f16x8{};  // Z columns 8 .. 15
+    if (G == 0) {  // Z columns 8 .. 15 of both buffers
+      *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + 16)) = f16x8{};
+      *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + kPT + 16)) = f16x8{};
+    }
 
     float m_run[4], l_part[4];  // heads 4G + i (the lane's S rows)
 #pragma unroll
@@ -246,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       return __builtin_amdgcn_ballot_w64(need) != 0;
     };
     // refresh the running maxima; the PV wave gets the per-head factor with the block
-    auto refresh = [&](f32x4 S) {
+    auto refresh = [&](f32x4 S, int so) {
       f32x4 alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -255,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         m_run[i] = m_new;
         l_part[i] *= alpha[i];
       }
-      if (L16 == 0) *reinterpret_cast<lds_ptr<f32x4>>(tb + (o_al + 16 * G)) = alpha;
+      if (L16 == 0) *reinterpret_cast<lds_ptr<f32x4>>(tb + (o_al + so + 16 * G)) = alpha;
     };
     // softmax of block t with the current running maxima, probabilities to the P tile, publish
-    auto publish = [&](f32x4 S, int t, bool resc) {
+    auto publish = [&](f32x4 S, int t, bool resc, int so) {
       f16x4 pz;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -267,14 +261,14 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         l_part[i] += e;
         pz[i] = (f16)e;
       }
-      *reinterpret_cast<lds_ptr<f16x4>>(tb + o_pwr) = pz;
-      if (lane == 0) fl[2] = resc ? 1 : 0;
+      *reinterpret_cast<lds_ptr<f16x4>>(tb + (o_pwr + so)) = pz;
+      if (lane == 0) *reinterpret_cast<lds_ptr<int>>(tb + (o_rs + so)) = resc ? 1 : 0;
       signal(fl + 0, t, lane);
     };
     // the QK of one block from K-step words kw(g) (C4 / RoPE: two dwords, C2: one), its scales and
     // zeros in mw (bf16 s | z << 16, 0 for masked tokens); writes the V, Z and SV tiles, returns S
     // (rows heads 4G + i, column token L16)
-    auto block_qk = [&](auto&& kw, auto&& kf16, const uint32_t* mw, bool valid, bool codes) -> f32x4 {
+    auto block_qk = [&](auto&& kw, auto&& kf16, const uint32_t* mw, bool valid, bool codes, int so) -> f32x4 {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
@@ -298,8 +292,8 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         c = mfma32k(qreg[2 * g + 1], k1, c);
         s += bf16f(mw[g] & 0xFFFFu) * c;
         if (g < 8) {
-          *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + 128 * g)) = k0;
-          *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + 128 * g + 16)) = k1;
+          *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + so + 128 * g)) = k0;
+          *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_vwr + so + 128 * g + 16)) = k1;
         }
       }
       // The token's zeros in fp16 (every lane holds its token's nine), the zero-term operand from
@@ -314,111 +308,72 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         const uint32_t a0 = (G & 1) ? mw[2] : mw[0], b0 = (G & 1) ? mw[6] : mw[4];
         const uint32_t a1 = (G & 1) ? mw[3] : mw[1], b1 = (G & 1) ? mw[7] : mw[5];
         const uint32_t m0 = (G & 2) ? b0 : a0, m1 = (G & 2) ? b1 : a1;
-        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G)) = (f16)bf16f(m0 & 0xFFFFu);
-        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + 64 * G + 32)) = (f16)bf16f(m1 & 0xFFFFu);
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G)) = (f16)bf16f(m0 & 0xFFFFu);
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G + 32)) = (f16)bf16f(m1 & 0xFFFFu);
         if (G == 0) {
-          *reinterpret_cast<lds_ptr<f16x8>>(tb + o_zwr) = zlo;
-          *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + 16)) = z8;
+          *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + so)) = zlo;
+          *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + so + 16)) = z8;
         }
       }
       return mfma32k(qz, zf, s * c_log2) + (valid ? 0.f : -__builtin_inff());
     };
 
     if (packed) {
-      // page ids through the constant address space: uniform index, so scalar loads the compiler
-      // waits for where the id is used (one block after it is requested)
+      // page ids through the constant address space: uniform index, so scalar loads
       typedef __attribute__((address_space(4))) const int32_t cint;
       cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages + page0);
-      auto page_id = [&](int t) -> int {
-        const int pg = bt[min(t, last)];
-        return (pg < 0 || pg >= p.num_pages) ? 0 : pg;  // contract violation: wrong values, no fault
-      };
-      // this lane's source offset and slot use for each content staging instruction
-      int coff[GE::CI];
-      bool cact[GE::CI];
-#pragma unroll
-      for (int i = 0; i < GE::CI; ++i) {
-        const int sl = 64 * i + lane, tt = sl / GE::RS, u = sl % GE::RS;
-        cact[i] = i < GE::CI - 1 || tt < kB;  // all lanes busy but in the last instruction
-        coff[i] = (16 * pr + tt) * GE::CB + 16 * min(u, GE::CU - 1);  // the padding slot repeats a unit
-      }
-      // block t (page page0 + min(t, last)) into zone t % 3; every block issues GE::LOADS instructions
-      auto stage = [&](int t, int pg) {
-        const uint8_t* base = p.pages + (int64_t)pg * GE::PB;
-        const uint8_t* srcR = base + GE::ROPE0 + 16 * pr * (kDr / 2);
-        const uint8_t* srcM = base + GE::META0 + 16 * pr * 4 * kGroups;
-        // The destination goes through an empty asm so that the compiler does not tie these loads
-        // to the staging array: its own waits would then hold every read of the array until all
-        // staging loads land.  The explicit vmcnt wait before a block is read orders them instead.
-        // (called after the publish of block t - 3, whose wait covered every read of this zone)
-        const lds_ptr<uint8_t> zone = lds_opaque(&s_stage[pr][t % kZones][0]);
-#pragma unroll
-        for (int i = 0; i < GE::CI; ++i)
-          if (cact[i])
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + coff[i]),
-                                             (__attribute__((address_space(3))) void*)(zone + 1024 * i), 16, 0, 0);
-        if (lane < GE::SR / 16)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(srcR + 16 * lane),
-                                           (__attribute__((address_space(3))) void*)(zone + GE::SC), 16, 0, 0);
-        if (lane < GE::SM / 16)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(srcM + 16 * lane),
-                                           (__attribute__((address_space(3))) void*)(zone + GE::SC + GE::SR), 16, 0, 0);
-      };
-      const int o_m = GE::SC + GE::SR + L16 * 4 * kGroups;  // + 4 per group
-      const int o_c = L16 * (16 * GE::RS) + (BITS_C == 4 ? 8 : 4) * G;
-      const int o_r = GE::SC + L16 * (kDr / 2) + 8 * G;
-      auto produce = [&](int t) -> f32x4 {
-        const int zo = (pr * kZones + t % kZones) * GE::SZ;
-        const int tok = (page0 + t) * kPageTokens + row;
-        const bool valid = tok >= p_lo && tok < p_hi;
-        // every LDS read of the block is issued before any arithmetic (the scheduler would otherwise
-        // sink the metadata reads below the MFMAs and leave the scale FMAs to the end)
-        uint32_t mw[kGroups];
+      // The packed bytes of one block this lane needs, straight from HBM into registers: its token
+      // row's K-step words of every group (C4 / RoPE: two dwords, C2: one) and the token's nine
+      // metadata words.  Every call issues the same loads (block index clamped), so the
+      // compiler's count of loads in flight stays exact.
+      struct BlockRegs {
         u32x2 kv[kGroups];
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          // (vector types: a struct load can be split into loads that lose their object)
-          if (g == 8) kv[g] = lds_load<u32x2>(sb + (zo + o_r));
-          else if (BITS_C == 4) kv[g] = lds_load<u32x2>(sb + (zo + o_c + 32 * g));
-          else kv[g] = u32x2{lds_load<uint32_t>(sb + (zo + o_c + 16 * g)), 0u};
-          mw[g] = lds_load<uint32_t>(sb + (zo + o_m + 4 * g));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) mw[g] = valid ? mw[g] : 0u;
-        auto kw = [&](int g) -> u32x2 { return kv[g]; };
-        auto none = [&](int, int) { return f16x8{}; };
-        return block_qk(kw, none, mw, valid, true);
+        uint32_t mw[kGroups];
       };
-      stage(0, page_id(0));
-      stage(1, page_id(1));
-      stage(2, page_id(2));
-      int pg_next = page_id(3);
-      load_queries();  // its latency overlaps the first blocks' staging
-      int t = 0;
-      f32x4 S;
-      while (true) {
-        bool held = false;
-        for (; t <= last; ++t) {
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GE::LOADS) : "memory");  // block t landed
-          wait_at_least(fl + 1, t - 1);  // the PV wave has taken block t - 1's tiles
-          S = produce(t);
-          if (needs_refresh(S)) {
-            held = true;
-            break;
-          }
-          publish(S, t, false);
-          stage(t + 3, pg_next);  // zone t % 3: block t's reads are done
-          pg_next = page_id(t + 4);
+      auto load = [&](int t, BlockRegs& R) {
+        int pg = bt[min(t, last)];
+        if (pg < 0 || pg >= p.num_pages) pg = 0;  // contract violation: wrong values, no fault
+        const uint8_t* base = p.pages + (int64_t)pg * GE::PB;
+        const uint8_t* crow = base + row * GE::CB + (BITS_C == 4 ? 8 : 4) * G;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (BITS_C == 4) R.kv[g] = *reinterpret_cast<const u32x2*>(crow + 32 * g);
+          else R.kv[g] = u32x2{*reinterpret_cast<const uint32_t*>(crow + 16 * g), 0u};
         }
-        if (!held) break;
-        refresh(S);  // rare: kept apart from the block loop
-        publish(S, t, true);
-        stage(t + 3, pg_next);
-        pg_next = page_id(t + 4);
-        ++t;
+        R.kv[8] = *reinterpret_cast<const u32x2*>(base + GE::ROPE0 + row * (kDr / 2) + 8 * G);
+        const uint32_t* mrow = reinterpret_cast<const uint32_t*>(base + GE::META0 + row * 4 * kGroups);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) R.mw[g] = mrow[g];
+      };
+      auto step = [&](int t, BlockRegs& R) {
+        if (t <= last) {
+          const int tok = (page0 + t) * kPageTokens + row;
+          const bool valid = tok >= p_lo && tok < p_hi;
+          uint32_t mw[kGroups];
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g) mw[g] = valid ? R.mw[g] : 0u;
+          auto kw = [&](int g) -> u32x2 { return R.kv[g]; };
+          auto none = [&](int, int) { return f16x8{}; };
+          const int so = (t & 1) * kPT;
+          wait_at_least(fl + 1, t - 2);  // the PV wave has read buffer t % 2 (block t - 2)
+          const f32x4 S = block_qk(kw, none, mw, valid, true, so);
+          const bool resc = needs_refresh(S);
+          if (resc) refresh(S, so);
+          publish(S, t, resc, so);
+        }
+        load(t + kAhead, R);  // the registers of block t now take block t + 3
+      };
+      BlockRegs R0, R1, R2;
+      load(0, R0);
+      load(1, R1);
+      load(2, R2);
+      load_queries();
+      for (int t = 0; t <= last; t += 3) {
+        step(t, R0);
+        step(t + 1, R1);
+        step(t + 2, R2);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no staging left in flight
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
     } else {
       // bf16 tokens in virtual pages of 64, the pair's rows 16 pr .. 16 pr + 15 of each.  With
       // several query tokens, this workgroup's query sees the first n_vis tokens (the ones it does
@@ -443,11 +398,12 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
           return __builtin_bit_cast(f16x8, g < 8 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw));
         };
         auto none = [&](int) { return u32x2{0u, 0u}; };
-        wait_at_least(fl + 1, t - 1);
-        const f32x4 S = block_qk(none, kf16, mw, valid, false);
+        const int so = (t & 1) * kPT;
+        wait_at_least(fl + 1, t - 2);  // buffer t % 2 is free
+        const f32x4 S = block_qk(none, kf16, mw, valid, false, so);
         const bool resc = needs_refresh(S);
-        if (resc) refresh(S);
-        publish(S, t, resc);
+        if (resc) refresh(S, so);
+        publish(S, t, resc, so);
       }
     }
     // ---- merge: this pair's running max and sum
@@ -472,16 +428,17 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
     f32x4 oz = {0.f, 0.f, 0.f, 0.f};  // rows z index 4G + i
     for (int t = 0; t < n_blocks; ++t) {
       wait_at_least(fl + 0, t);  // block t published
-      // block t's operands into registers (k = tokens 4G .. 4G + 3), then release the tiles
-      const f16x4 pb = lds_tr4((lds_ptr<f16>)(tb + o_ptr));  // B: head L16
-      const f16x4 za = lds_tr4((lds_ptr<f16>)(tb + o_ztr));  // A: z index L16
+      // block t's operands into registers (k = tokens 4G .. 4G + 3), then release its buffer
+      const int so = (t & 1) * kPT;
+      const f16x4 pb = lds_tr4((lds_ptr<f16>)(tb + (o_ptr + so)));  // B: head L16
+      const f16x4 za = lds_tr4((lds_ptr<f16>)(tb + (o_ztr + so)));  // A: z index L16
       f16x4 sv[8], va[32];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) sv[g] = lds_load<f16x4>(tb + (o_svr + 32 * g));
+      for (int g = 0; g < 8; ++g) sv[g] = lds_load<f16x4>(tb + (o_svr + so + 32 * g));
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) va[cb] = lds_tr4((lds_ptr<f16>)(tb + (o_vtr + 32 * cb)));
-      const int resc = __builtin_amdgcn_readfirstlane(fl[2]);
-      const float alpha = lds_load<float>(tb + (o_al + 4 * L16));
+      for (int cb = 0; cb < 32; ++cb) va[cb] = lds_tr4((lds_ptr<f16>)(tb + (o_vtr + so + 32 * cb)));
+      const int resc = __builtin_amdgcn_readfirstlane(lds_load<int>(tb + (o_rs + so)));
+      const float alpha = lds_load<float>(tb + (o_al + so + 4 * L16));
       signal(fl + 1, t, lane);
       if (resc) {
 #pragma unroll
