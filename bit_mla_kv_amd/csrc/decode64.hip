@@ -506,15 +506,6 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         const int sl = (k - 1) % kSlots, pb = (k - 1) & 1;
         const lds_ptr<f16> tb = lds_opaque(&sm.tile[sl][0]);
         const lds_ptr<int> rf = lds_opaque(&sm.resc[pb][0]);
-        if (rf[0] | rf[1] | rf[2] | rf[3]) {
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const float a = sm.alpha[pb][32 * hb + l32];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) O[hb][cb] *= a;
-          }
-          oz *= sm.alpha[pb][16 * v + L16];
-        }
         const lds_ptr<f16> ptb = lds_opaque(&sm.probT[pb][0][0]);
         // request every operand of the step before multiplying (the fence keeps them together)
         // zero-term sums for heads 16v + L16 (A: z rows from the zero-term columns, k: tokens
@@ -535,6 +526,16 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           for (int cb = 0; cb < 4; ++cb) A[ks][cb] = cat(lds_tr4(va + 32 * cb), lds_tr4(va + 8 * kS + 32 * cb));
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) P[ks][hb] = cat(lds_tr4(pbp + 32 * hb), lds_tr4(pbp + 8 * kPT + 32 * hb));
+        }
+        // the refresh flags are read with the operands, so one wait covers both
+        if (rf[0] | rf[1] | rf[2] | rf[3]) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const float a = sm.alpha[pb][32 * hb + l32];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) O[hb][cb] *= a;
+          }
+          oz *= sm.alpha[pb][16 * v + L16];
         }
         __builtin_amdgcn_sched_barrier(0);
         oz = mfma16(zA, zP, oz);
