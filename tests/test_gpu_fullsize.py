@@ -69,3 +69,47 @@ def test_full_size_sampled(name):
         assert E.max() <= E_TOL, f"{name} seq {b} heads {heads}: E {E}"
         err = np.abs(l_all[b, heads] - rl)
         assert err.max() <= LSE_TOL, f"{name} seq {b} heads {heads}: lse err {err}"
+
+
+def test_full_size_multi_query():
+    """Four query tokens per sequence on the 16-head 128K workload (the queries share one read of
+    the cache as one 64-row group): sampled sequences, every query, sampled heads; query i sees the
+    first N - (3 - i) tokens in the representation the cache holds at length N."""
+    w = mi.workload("dsv2lite_c4r4_128k")
+    B, H, QL = w.batch, w.heads, 4
+    dev = torch.device("cuda:0")
+    lens = w.seq_lens.astype(np.int64)
+    layout = m.make_layout(w.bits_c)
+    cache = cb.allocate_for(layout, lens, mi.page_permutation(w.seed, int(((lens + 63) // 64).sum()) + 8), device=dev)
+    outl = mi.outlier_channels(w.seed)
+    seqs = [0, B - 1]
+    kept = {}
+    for b in range(B):
+        rows = mi.rows(w.seed, b, int(lens[b]), outl, threads=16)
+        cb.prefill(cache, b, rows)
+        if b in seqs:
+            kept[b] = rows
+        del rows
+    q_host = mi.queries(w.seed + 7, B * QL, H).reshape(B, QL, H, 576)
+    q = cb.to_device_bf16(q_host.reshape(B * QL * H, -1), dev).view(B, QL, H, 576)
+    out = torch.empty((B, QL, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, QL, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(layout, B, QL * H, int(lens.max()), dev)
+    m.decode_multi(cache, q, torch.arange(B, dtype=torch.int32, device=dev),
+                   torch.tensor(lens, dtype=torch.int32, device=dev), int(lens.max()), w.scale, out, lse, ws)
+    torch.cuda.synchronize()
+    o_all = bf16_tensor_to_f64(out)
+    l_all = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all))
+    pick = np.random.default_rng(2000 + w.seed)
+    for b in seqs:
+        rows = kept[b]
+        n = rows.shape[0]
+        cc, cr, meta = oracle.quantize(rows, w.bits_c)
+        sel = oracle.select(rows, cc, cr, meta, w.bits_c)
+        heads = sorted({0, H - 1, int(pick.integers(H))})
+        for i in range(QL):
+            ro, rl = oracle.attend(sel[: n - (QL - 1 - i)], q_host[b, i], w.scale, heads=heads)
+            E = e_metric(o_all[b, i, heads], ro)
+            assert E.max() <= E_TOL, f"seq {b} query {i} heads {heads}: E {E}"
+            assert np.abs(l_all[b, i, heads] - rl).max() <= LSE_TOL, f"seq {b} query {i}"
