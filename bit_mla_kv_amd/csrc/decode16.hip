@@ -11,28 +11,27 @@
 // (waves r and r + 4) owns rows 16r..16r+15 of every page of the split; the
 // pair's two waves split the work by role and run concurrently, so one wave's
 // stalls are covered by other waves' work:
-//  - the QK wave streams the pair's 16-token block of each page (packed codes,
-//    RoPE codes, metadata) with global_load_lds_dwordx4 into its three-zone LDS
-//    ring (blocks t+1, t+2 in flight while t is read).  A token's content row
-//    takes one more 16-byte slot than it needs (the loader lanes of that slot
-//    are masked off), so the 16 rows start in different banks and a column of
-//    them reads conflict-free.  QK: MFMA 16x16x32 f16, queries as the A
-//    operand, the exact codes of the block as the B operand (nibbles / crumbs
-//    become fp8 bytes whose e4m3 value is code * 2^-9, converted with a 2^9
-//    scale); each lane owns one token, so a group's fp32 scale is one scalar;
-//    the zero terms of all nine groups go through one more MFMA.  Online
-//    softmax in the log2 domain with a lazily refreshed running max.  The
-//    unpacked content codes, zeros, PV scales and fp16 probabilities of the
-//    block go to the pair's LDS tiles;
-//  - the PV wave takes the block's operands from the tiles (transposed reads,
-//    ds_read_b64_tr_b16) into registers, hands the tiles back, and accumulates
+//  - the QK wave loads, for each 16-token block of the pair, its lanes' packed
+//    words straight from HBM into registers three blocks ahead (the K-step
+//    words of the lane's token row for every group, and the token's nine
+//    metadata words).  QK: MFMA 16x16x32 f16, queries as the A operand, the
+//    exact codes of the block as the B operand (nibbles / crumbs become fp8
+//    bytes whose e4m3 value is code * 2^-9, converted with a 2^9 scale); each
+//    lane owns one token, so a group's fp32 scale is one scalar; the zero
+//    terms of all nine groups go through one more MFMA.  Online softmax in the
+//    log2 domain with a lazily refreshed running max.  The unpacked content
+//    codes, zeros, PV scales and fp16 probabilities of block t go to the pair's
+//    tile buffer t % 2;
+//  - the PV wave takes the block's operands from that buffer (transposed
+//    reads, ds_read_b64_tr_b16) into registers, releases it, and accumulates
 //    MFMA 16x16x16 f16 of the codes against p * s_g, plus sum_t p_t z_g,t.
-// The two waves hand each block over through LDS sequence flags (the QK wave
-// publishes block t once its tiles are written, the PV wave releases them once
-// its operands are in registers); every wait is bounded, so a broken handshake
-// gives wrong values, never a hang.  The four pairs' partials are merged
-// through LDS at the end; the split's partial stays unnormalised with its
-// running max and sum for the combine.
+// The two waves hand blocks over through LDS sequence flags: the QK wave
+// publishes block t once its buffer is written, and writes block t only after
+// the PV wave has released block t - 2 (two buffers), so it runs up to a block
+// ahead.  Every wait is bounded, so a broken handshake gives wrong values,
+// never a hang.  The four pairs' partials are merged through LDS at the end;
+// the split's partial stays unnormalised with its running max and sum for the
+// combine.
 #include <algorithm>
 #include <cstddef>
 
