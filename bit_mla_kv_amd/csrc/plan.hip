@@ -133,9 +133,38 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     bf_base += tb;
   }
   const int F = full_base, T = tail_base, BF = bf_base;
+
+  // Tail chunks longest first: the hardware starts workgroups in item order as CUs free up, so
+  // this is greedy longest-processing-time scheduling of the tails after the equal full chunks.
+  // A tail's position is its rank by (pages descending, sequence ascending); computed in lane
+  // registers for up to kTailSortMax sequences, otherwise the tails stay in sequence order.
+  constexpr int kTailSortMax = 4 * kPlanThreads;
+  int tail_pages[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = t + kPlanThreads * k;
+    int fp;
+    tail_pages[k] = (b < p.batch && p.batch <= kTailSortMax) ? seq_packed_pages(p, b, &fp) % pps : 0;
+  }
+  const int n_groups = p.batch <= kTailSortMax ? (p.batch + kPlanThreads - 1) / kPlanThreads : 0;
+  int ranks[4] = {0, 0, 0, 0};  // rank of the tail of sequence t + 64 k among all tails
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) {
+    if (k2 >= n_groups) break;
+    for (int src = 0; src < kPlanThreads; ++src) {
+      const int other = __builtin_amdgcn_readlane(tail_pages[k2], src), b2 = src + kPlanThreads * k2;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int mine = tail_pages[k], b = t + kPlanThreads * k;
+        ranks[k] += other > mine || (other == mine && other > 0 && b2 < b);
+      }
+    }
+  }
   // pass 2: emit items (b, first page, pages, kind)
   for (int b = t; b < p.batch; b += kPlanThreads) {
-    const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1], tl = p.seq_info[4 * b + 2];
+    const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
+    int tl = p.seq_info[4 * b + 2];
+    if (tl >= 0 && p.batch <= kTailSortMax) tl = ranks[(b - t) / kPlanThreads];
     const int bo = F + T + p.seq_info[4 * b + 3];
     int fp;
     const int n = seq_packed_pages(p, b, &fp);
