@@ -382,19 +382,22 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       for (int t = 0; t < n_blocks; ++t) {
         const int j = jb + t * kPageTokens + row;
         const bool valid = j < nb && (j < ns ? j : rstart + (j - ns)) < n_vis;
-        const uint16_t* src = nullptr;  // masked lanes read nothing
-        if (valid) {
-          if (j < ns) src = p.sink + ((int64_t)slot * p.n_sink + j) * kD;
-          else src = p.recent + ((int64_t)slot * p.n_recent + (rstart + (j - ns)) % p.n_recent) * kD;
-        }
+        // every lane loads (rows past the list or not seen read the slot's first recent row and are
+        // dropped), so that the block's 18 loads are issued together
+        const bool in = j < nb;
+        const uint16_t* src = p.recent + (int64_t)slot * p.n_recent * kD;
+        if (in && j < ns) src = p.sink + ((int64_t)slot * p.n_sink + j) * kD;
+        else if (in) src = p.recent + ((int64_t)slot * p.n_recent + (rstart + (j - ns)) % p.n_recent) * kD;
+        uint4 raw[2 * kGroups];
+#pragma unroll
+        for (int k = 0; k < 2 * kGroups; ++k) raw[k] = *reinterpret_cast<const uint4*>(src + 64 * (k >> 1) + 16 * G + 8 * (k & 1));
         // scale 1 (bf16 0x3F80) and zero 0 for valid tokens
         uint32_t mw[kGroups];
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) mw[g] = valid ? 0x3F80u : 0u;
         auto kf16 = [&](int g, int h) -> f16x8 {
-          uint4 raw = make_uint4(0, 0, 0, 0);
-          if (valid) raw = *reinterpret_cast<const uint4*>(src + 64 * g + 16 * G + 8 * h);
-          return __builtin_bit_cast(f16x8, g < 8 ? bf16_chunk_to_f16<BITS_C>(raw) : bf16_chunk_to_f16<4>(raw));
+          const uint4 r = valid ? raw[2 * g + h] : make_uint4(0, 0, 0, 0);
+          return __builtin_bit_cast(f16x8, g < 8 ? bf16_chunk_to_f16<BITS_C>(r) : bf16_chunk_to_f16<4>(r));
         };
         auto none = [&](int) { return u32x2{0u, 0u}; };
         const int so = (t & 1) * kPT;

@@ -5,10 +5,11 @@
 // is cut into page-aligned chunks of one common size P = ceil(total pages /
 // target items), and its list of bf16 (sink + recent) tokens into chunks of
 // 64 P tokens (one item when, as usual, there are at most 132; many when the
-// recent window is long).  Items are ordered full chunks first, then the
-// shorter tail chunks, then the bf16 chunks, so the hardware's in-order
-// dispatch starts the longest work first.  When a slightly longer chunk lets
-// every item run at once (one round of workgroups), that chunk is used.  combine_kernel merges each
+// recent window is long).  Items are ordered bf16 chunks first (short: their
+// CUs go on to packed work), then the full chunks, then the tail chunks
+// longest first, so the hardware's in-order dispatch is a greedy
+// longest-first schedule of the packed work.  When a slightly longer chunk lets
+// every packed item run at once (one round of workgroups), that chunk is used.  combine_kernel merges each
 // sequence's partial results exactly (max-shifted sums), adding the deferred
 // zero terms, and writes bf16 outputs and natural-log lse.
 #include <algorithm>
@@ -70,9 +71,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   const long long total = local;
   int pps = (int)std::min<long long>((total + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
-  // target_items workgroups run at once.  Full chunks plus tails plus the bf16 items can exceed it
-  // by up to 2 x batch, and the excess then runs as a second round after a full chunk.  When a
-  // chunk at most a quarter longer brings every item into one round, take the shortest such chunk.
+  // target_items workgroups run at once.  Full chunks plus tails can exceed it by up to batch, and
+  // the excess then runs as a second round after a full chunk.  When a chunk at most a quarter
+  // longer brings every packed item into one round, take the shortest such chunk.
   if (p.batch <= kPlanThreads * kPlanRegs && 2 * p.batch <= p.target_items) {
     int n_reg[kPlanRegs], f_reg[kPlanRegs];
     int n_max = 0;
@@ -86,10 +87,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
-    auto items_at = [&](int c) {  // all items of a plan with chunks of c pages
+    // packed items of a plan with chunks of c pages (the bf16 items are short and run first, so
+    // their CUs go on to packed chunks: they do not take a slot of the round)
+    auto items_at = [&](int c) {
       int n = 0;
 #pragma unroll
-      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c + (f_reg[k] >= 0 ? bf16_items(f_reg[k], c) : 0);
+      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c;
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
       return n;
@@ -165,15 +168,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
     int tl = p.seq_info[4 * b + 2];
     if (tl >= 0 && p.batch <= kTailSortMax) tl = ranks[(b - t) / kPlanThreads];
-    const int bo = F + T + p.seq_info[4 * b + 3];
+    const int bo = p.seq_info[4 * b + 3];
     int fp;
     const int n = seq_packed_pages(p, b, &fp);
     // capacity guards only matter when a caller breaks the seq_len <= max_seq_len contract
-    for (int k = 0; k < nf && fo + k < p.max_items; ++k)
-      reinterpret_cast<int4*>(p.items)[fo + k] = make_int4(b, fp + k * pps, pps, 0);
+    for (int k = 0; k < nf && BF + fo + k < p.max_items; ++k)
+      reinterpret_cast<int4*>(p.items)[BF + fo + k] = make_int4(b, fp + k * pps, pps, 0);
     if (tl >= 0) {
-      if (F + tl < p.max_items) reinterpret_cast<int4*>(p.items)[F + tl] = make_int4(b, fp + nf * pps, n - nf * pps, 0);
-      p.seq_info[4 * b + 2] = F + tl < p.max_items ? F + tl : -1;
+      const int ti = BF + F + tl;
+      if (ti < p.max_items) reinterpret_cast<int4*>(p.items)[ti] = make_int4(b, fp + nf * pps, n - nf * pps, 0);
+      p.seq_info[4 * b + 2] = ti < p.max_items ? ti : -1;
     }
     // bf16 chunks (first index into the sequence's bf16 token list, count)
     const int nbt = seq_bf16_tokens(p, b), chunk = pps * kPageTokens;
@@ -181,7 +185,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     for (int k = 0; k < nbi && bo + k < p.max_items; ++k)
       reinterpret_cast<int4*>(p.items)[bo + k] = make_int4(b, k * chunk, min(chunk, nbt - k * chunk), 1);
     p.seq_info[4 * b + 3] = bo < p.max_items ? bo : -1;  // first bf16 item
-    if (fo + nf > p.max_items) p.seq_info[4 * b + 1] = max(0, p.max_items - fo);
+    p.seq_info[4 * b + 0] = BF + fo;
+    if (BF + fo + nf > p.max_items) p.seq_info[4 * b + 1] = max(0, p.max_items - BF - fo);
   }
   if (t == 0) {
     p.plan_hdr[0] = F + T + BF;  // item count
