@@ -58,41 +58,51 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
   return x - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
-  const int t = threadIdx.x;
-  // total packed pages
+// The plan for batch <= kPlanThreads * kPlanRegs: every sequence's length is read once into lane
+// registers (sequence t + 64 k in register k), and both passes run on them.
+__device__ void plan_in_registers(const DecodeParams& p, int t) {
+  constexpr int R = kPlanRegs;
+  int fpg[R], npk[R], nbt[R];
+  bool has[R];
+  int Nv[R], sv[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {  // all loads first: one round trip
+    const int b = t + kPlanThreads * k;
+    has[k] = b < p.batch;
+    Nv[k] = has[k] ? p.seq_len[b] : 0;
+    sv[k] = has[k] ? p.seq_slot[b] : 0;
+  }
   long long local = 0;
-  for (int b = t; b < p.batch; b += kPlanThreads) {
-    int fp;
-    local += seq_packed_pages(p, b, &fp) + seq_bf16_pages(p, b);
+  int n_max = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int N = (sv[k] < 0 || sv[k] >= p.num_slots) ? 0 : Nv[k];
+    const int p_lo = p.n_sink, p_hi = N - p.n_recent;
+    fpg[k] = p_lo / kPageTokens;
+    npk[k] = has[k] && p_hi > p_lo ? (p_hi - 1) / kPageTokens - fpg[k] + 1 : 0;
+    nbt[k] = has[k] ? bf16_token_count(N, p.n_sink, p.n_recent) : 0;
+    local += npk[k] + (nbt[k] + kPageTokens - 1) / kPageTokens;
+    n_max = std::max(n_max, npk[k]);
   }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
-  const long long total = local;
-  int pps = (int)std::min<long long>((total + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
+  for (int d = 32; d >= 1; d >>= 1) {
+    local += __shfl_xor(local, d, 64);
+    n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
+  }
+  int pps = (int)std::min<long long>((local + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
   // target_items workgroups run at once.  Full chunks plus tails can exceed it by up to batch, and
   // the excess then runs as a second round after a full chunk.  When a chunk at most a quarter
-  // longer brings every packed item into one round, take the shortest such chunk.
-  if (p.batch <= kPlanThreads * kPlanRegs && 2 * p.batch <= p.target_items) {
-    int n_reg[kPlanRegs], f_reg[kPlanRegs];
-    int n_max = 0;
-#pragma unroll
-    for (int k = 0; k < kPlanRegs; ++k) {
-      const int b = t + kPlanThreads * k;
-      int fp;
-      n_reg[k] = b < p.batch ? seq_packed_pages(p, b, &fp) : 0;
-      f_reg[k] = b < p.batch ? seq_bf16_pages(p, b) : -1;  // -1: no sequence, no bf16 item
-      n_max = std::max(n_max, std::max(n_reg[k], f_reg[k]));
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
-    // packed items of a plan with chunks of c pages (the bf16 items are short and run first, so
-    // their CUs go on to packed chunks: they do not take a slot of the round)
+  // longer brings every packed item into one round, take the shortest such chunk (the bf16 items
+  // are short and run first, so their CUs go on to packed chunks: they take no slot of the round).
+  if (2 * p.batch <= p.target_items) {
     auto items_at = [&](int c) {
       int n = 0;
 #pragma unroll
-      for (int k = 0; k < kPlanRegs; ++k) n += (n_reg[k] + c - 1) / c;
+      for (int k = 0; k < R; ++k) {
+        if (kPlanThreads * k >= p.batch) break;  // (integer divisions are not cheap)
+        n += (npk[k] + c - 1) / c;
+      }
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
       return n;
@@ -107,6 +117,99 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
       pps = hi;
     }
   }
+  if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
+
+  // pass 1: per-sequence item counts and their offsets (scans over each group of 64 sequences)
+  int fo[R], nf[R], tl[R], tp[R], nbi[R], bo[R];
+  int full_base = 0, tail_base = 0, bf_base = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (kPlanThreads * k >= p.batch) {
+      nf[k] = tp[k] = nbi[k] = fo[k] = tl[k] = bo[k] = 0;
+      continue;
+    }
+    nf[k] = npk[k] / pps;
+    tp[k] = npk[k] - nf[k] * pps;  // tail pages (0: no tail)
+    nbi[k] = has[k] ? bf16_items((nbt[k] + kPageTokens - 1) / kPageTokens, pps) : 0;
+    int tf, tt, tb;
+    const int of = wave_exclusive_scan(nf[k], &tf);
+    const int ot = wave_exclusive_scan(tp[k] != 0, &tt);
+    const int ob = wave_exclusive_scan(nbi[k], &tb);
+    fo[k] = full_base + of;
+    tl[k] = tail_base + ot;  // sequence order, replaced by the longest-first rank below
+    bo[k] = bf_base + ob;
+    full_base += tf;
+    tail_base += tt;
+    bf_base += tb;
+  }
+  const int F = full_base, T = tail_base, BF = bf_base;
+  // Tail chunks longest first: the hardware starts workgroups in item order as CUs free up, so
+  // this is greedy longest-processing-time scheduling of the tails after the equal full chunks.
+  // A tail's position is its rank by (pages descending, sequence ascending), for up to
+  // kTailSortMax sequences (otherwise the tails keep sequence order).
+  constexpr int kTailSortMax = 4 * kPlanThreads;
+  if (p.batch <= kTailSortMax) {
+    const int n_groups = (p.batch + kPlanThreads - 1) / kPlanThreads;
+    int ranks[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      if (k2 >= n_groups) break;
+      const int n_src = min(kPlanThreads, p.batch - kPlanThreads * k2);
+      for (int src = 0; src < n_src; ++src) {
+        const int other = __builtin_amdgcn_readlane(tp[k2], src), b2 = src + kPlanThreads * k2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int mine = tp[k], b = t + kPlanThreads * k;
+          ranks[k] += other > mine || (other == mine && other > 0 && b2 < b);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tl[k] = ranks[k];
+  }
+  // pass 2: emit items (b, first page, pages, kind): bf16 chunks, full chunks, tails
+  const int chunk = pps * kPageTokens;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (!has[k]) continue;
+    const int b = t + kPlanThreads * k;
+    // capacity guards only matter when a caller breaks the seq_len <= max_seq_len contract
+    for (int j = 0; j < nf[k] && BF + fo[k] + j < p.max_items; ++j)
+      reinterpret_cast<int4*>(p.items)[BF + fo[k] + j] = make_int4(b, fpg[k] + j * pps, pps, 0);
+    int ti = -1;
+    if (tp[k] != 0) {
+      ti = BF + F + tl[k];
+      if (ti < p.max_items) reinterpret_cast<int4*>(p.items)[ti] = make_int4(b, fpg[k] + nf[k] * pps, tp[k], 0);
+      else ti = -1;
+    }
+    for (int j = 0; j < nbi[k] && bo[k] + j < p.max_items; ++j)
+      reinterpret_cast<int4*>(p.items)[bo[k] + j] = make_int4(b, j * chunk, min(chunk, nbt[k] - j * chunk), 1);
+    const int nf_cap = BF + fo[k] + nf[k] > p.max_items ? max(0, p.max_items - BF - fo[k]) : nf[k];
+    reinterpret_cast<int4*>(p.seq_info)[b] = make_int4(BF + fo[k], nf_cap, ti, bo[k] < p.max_items ? bo[k] : -1);
+  }
+  if (t == 0) {
+    p.plan_hdr[0] = F + T + BF;  // item count
+    p.plan_hdr[1] = pps;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
+  const int t = threadIdx.x;
+  if (p.batch <= kPlanThreads * kPlanRegs) {
+    plan_in_registers(p, t);
+    return;
+  }
+  // larger batches: the sequences are read per pass, chunks of P = ceil(total pages / target
+  // items) pages, tails in sequence order
+  long long local = 0;
+  for (int b = t; b < p.batch; b += kPlanThreads) {
+    int fp;
+    local += seq_packed_pages(p, b, &fp) + seq_bf16_pages(p, b);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
+  int pps = (int)std::min<long long>((local + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
+  pps = std::max(pps, p.min_pages_per_split);
   if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
 
   // pass 1: counts of full / tail / bf16 items, scanned in chunks of 64 sequences (lane t owns
@@ -136,38 +239,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     bf_base += tb;
   }
   const int F = full_base, T = tail_base, BF = bf_base;
-
-  // Tail chunks longest first: the hardware starts workgroups in item order as CUs free up, so
-  // this is greedy longest-processing-time scheduling of the tails after the equal full chunks.
-  // A tail's position is its rank by (pages descending, sequence ascending); computed in lane
-  // registers for up to kTailSortMax sequences, otherwise the tails stay in sequence order.
-  constexpr int kTailSortMax = 4 * kPlanThreads;
-  int tail_pages[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int b = t + kPlanThreads * k;
-    int fp;
-    tail_pages[k] = (b < p.batch && p.batch <= kTailSortMax) ? seq_packed_pages(p, b, &fp) % pps : 0;
-  }
-  const int n_groups = p.batch <= kTailSortMax ? (p.batch + kPlanThreads - 1) / kPlanThreads : 0;
-  int ranks[4] = {0, 0, 0, 0};  // rank of the tail of sequence t + 64 k among all tails
-#pragma unroll
-  for (int k2 = 0; k2 < 4; ++k2) {
-    if (k2 >= n_groups) break;
-    for (int src = 0; src < kPlanThreads; ++src) {
-      const int other = __builtin_amdgcn_readlane(tail_pages[k2], src), b2 = src + kPlanThreads * k2;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int mine = tail_pages[k], b = t + kPlanThreads * k;
-        ranks[k] += other > mine || (other == mine && other > 0 && b2 < b);
-      }
-    }
-  }
   // pass 2: emit items (b, first page, pages, kind)
   for (int b = t; b < p.batch; b += kPlanThreads) {
     const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
-    int tl = p.seq_info[4 * b + 2];
-    if (tl >= 0 && p.batch <= kTailSortMax) tl = ranks[(b - t) / kPlanThreads];
+    const int tl = p.seq_info[4 * b + 2];
     const int bo = p.seq_info[4 * b + 3];
     int fp;
     const int n = seq_packed_pages(p, b, &fp);

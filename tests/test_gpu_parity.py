@@ -218,6 +218,22 @@ def test_decode_many_sequences(heads):
     check(out, lse, ro, rl, f"B130 H{heads}")
 
 
+@pytest.mark.parametrize("heads", [16, 64])
+def test_decode_large_batch_plan(heads):
+    """600 sequences: above the planner's register path (512), so its per-pass path runs;
+    also 300 (register path, tails in sequence order above 256)."""
+    for B in (600, 300):
+        rng = np.random.default_rng(49 + heads + B)
+        lens = [int(x) for x in rng.integers(0, 400, size=B)]
+        lens[0], lens[B - 1] = 0, 700
+        rows = [mi.rows(49, b, n) for b, n in enumerate(lens)]
+        q = mi.queries(49, B, heads)
+        cache = build(rows, 4, seed=49)
+        out, lse = run_decode(cache, q, lens)
+        ro, rl = reference(rows, q, 4, SCALE)
+        check(out, lse, ro, rl, f"B{B} H{heads}")
+
+
 def test_decode_heads_256():
     lens = [900, 3000]
     rows = [mi.rows(41, b, n) for b, n in enumerate(lens)]
