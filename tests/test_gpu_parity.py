@@ -337,6 +337,25 @@ def test_decode_multi_single_query_is_decode():
     assert torch.equal(o1, o2.view(2, 16, 512)) and torch.equal(l1, l2.view(2, 16))
 
 
+@pytest.mark.parametrize("n_sink,n_recent", [(0, 1), (0, 128), (64, 16), (7, 200)])
+@pytest.mark.parametrize("heads", [16, 64])
+def test_decode_window_layouts(n_sink, n_recent, heads):
+    """Other sink / recent windows of the layout: no sink, a one-token recent window, the largest
+    sink; writer bytes bit-exact and decode against the oracle with the same windows."""
+    lens = [0, 1, 5, 63, 64, 65, 300, 1000]
+    rows = [mi.rows(50, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(50, len(lens), heads)
+    cache = build(rows, 4, seed=50, n_sink=n_sink, n_recent=n_recent)
+    check_bf16_buffers(cache, rows, n_sink=n_sink, n_recent=n_recent)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = [], []
+    for b, r in enumerate(rows):
+        o, l = oracle.decode_sequence(r, q[b], SCALE, 4, None, n_sink, n_recent)
+        ro.append(o)
+        rl.append(l)
+    check(out, lse, np.stack(ro), np.stack(rl), f"sink {n_sink} recent {n_recent} H{heads}")
+
+
 def test_exactly_once_canaries():
     """NaN in every representation a token must NOT be read from leaves the output unchanged."""
     lens = [1000, 150, 2, 0]
