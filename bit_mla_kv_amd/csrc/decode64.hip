@@ -145,14 +145,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + __shfl_xor(v, 8, 64);
 }
 
-// Scalar (SMEM) read of a wave-uniform int: it counts on lgkmcnt, so waiting for it leaves the
-// vector loads of staged tiles in flight.
-__device__ __forceinline__ int scalar_load(const int32_t* ptr) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
-}
-
 template <int BITS_C>
 __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   using GE = Geo<BITS_C>;
