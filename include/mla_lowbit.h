@@ -195,8 +195,9 @@ int mla_lowbit_decode_multi(const mla_lowbit_cache* cache, const void* q, const 
 
 /*
  * Measurement aid (not needed for decoding).  Arms two caller-created HIP
- * events (hipEvent_t passed as void*) for the NEXT mla_lowbit_decode call on
- * this thread: that call records `start` on its stream immediately before
+ * events (hipEvent_t passed as void*) for the NEXT mla_lowbit_decode or
+ * mla_lowbit_decode_multi call on this thread: that call records `start` on
+ * its stream immediately before
  * the split-KV decode kernel and `stop` immediately after it (before the
  * log-sum-exp combine), so hipEventElapsedTime(start, stop) is that kernel's
  * duration.  The events are disarmed after that call (also when it fails).
