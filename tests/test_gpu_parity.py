@@ -327,6 +327,28 @@ def test_decode_multi_query(heads, q_len):
     check(out, lse, ro, rl, f"multi H{heads} q_len {q_len}")
 
 
+@pytest.mark.parametrize("bits_c", [4, 2])
+def test_decode_multi_query_window_limit(bits_c):
+    """q_len = n_recent + 1 (the largest allowed): with a 3-token recent window, four queries;
+    the tokens the early queries do not see are exactly the window's, and the window is shorter
+    than the queries' spread for the first one."""
+    lens = [1, 4, 9, 70, 300]
+    rows = [mi.rows(51, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(51, len(lens) * 4, 16).reshape(len(lens), 4, 16, 576)
+    cache = build(rows, bits_c, seed=51, n_recent=3)
+    out, lse = run_decode_multi(cache, q, lens)
+    ro = np.zeros((len(lens), 4, 16, 512))
+    rl = np.full((len(lens), 4, 16), -np.inf)
+    for b, r in enumerate(rows):
+        cc, cr, meta = oracle.quantize(r, bits_c)
+        sel = oracle.select(r, cc, cr, meta, bits_c, 4, 3)
+        for i in range(4):
+            n_vis = r.shape[0] - (3 - i)
+            if n_vis > 0:
+                ro[b, i], rl[b, i] = oracle.attend(sel[:n_vis], q[b, i], SCALE)
+    check(out, lse, ro, rl, f"multi window limit C{bits_c}")
+
+
 def test_decode_multi_single_query_is_decode():
     lens = [700, 2049]
     rows = [mi.rows(48, b, n) for b, n in enumerate(lens)]
