@@ -113,3 +113,44 @@ def test_full_size_multi_query():
             E = e_metric(o_all[b, i, heads], ro)
             assert E.max() <= E_TOL, f"seq {b} query {i} heads {heads}: E {E}"
             assert np.abs(l_all[b, i, heads] - rl).max() <= LSE_TOL, f"seq {b} query {i}"
+
+
+@pytest.mark.parametrize("heads,bits_c", [(128, 4), (16, 2)])
+def test_million_token_context(heads, bits_c):
+    """The longest context of the pages' latency sweep (1M tokens), beside a short sequence in the
+    same batch: one 1,048,576-token sequence and one of 777 tokens, decoded with the default split
+    plan (the long one split over every CU, the short one in one or two items).  Sampled heads of
+    both sequences against the oracle, same bounds as above."""
+    seed = 11 + bits_c
+    lens = np.array([1 << 20, 777], np.int64)
+    B = len(lens)
+    dev = torch.device("cuda:0")
+    layout = m.make_layout(bits_c)
+    perm = mi.page_permutation(seed, int(((lens + 63) // 64).sum()))
+    cache = cb.allocate_for(layout, lens, perm, device=dev)
+    outl = mi.outlier_channels(seed)
+    kept = {}
+    for b in range(B):
+        kept[b] = mi.rows(seed, b, int(lens[b]), outl, threads=16)
+        cb.prefill(cache, b, kept[b])
+    q_host = mi.queries(seed, B, heads)
+    q = cb.to_device_bf16(q_host.reshape(B * heads, -1), dev).view(B, heads, 576)
+    out = torch.empty((B, heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, heads), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(layout, B, heads, int(lens.max()), dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    scale = float(np.float32(1.0 / np.sqrt(192.0)))
+    m.decode(cache, q, slots, torch.tensor(lens, dtype=torch.int32, device=dev), int(lens.max()), scale,
+             out, lse, ws)
+    torch.cuda.synchronize()
+    o_all = bf16_tensor_to_f64(out)
+    l_all = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all))
+    pick = np.random.default_rng(2000 + seed)
+    for b in range(B):
+        hs = sorted({0, heads - 1, int(pick.integers(heads))})
+        ro, rl = oracle.decode_sequence(kept[b], q_host[b], scale, bits_c, heads=hs)
+        E = e_metric(o_all[b, hs], ro)
+        assert E.max() <= E_TOL, f"H{heads} C{bits_c} seq {b} heads {hs}: E {E}"
+        err = np.abs(l_all[b, hs] - rl)
+        assert err.max() <= LSE_TOL, f"H{heads} C{bits_c} seq {b} heads {hs}: lse err {err}"
