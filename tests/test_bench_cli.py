@@ -12,3 +12,29 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_algorithmic_work_of_the_headline_decode():
+    """The roofline's algorithmic bytes and flops, worked by hand for 8 sequences of 131,072 tokens
+    and 128 heads: per packed token 256 B of 4-bit content, 32 B of 4-bit RoPE key and 9 x 4 B of
+    bf16 scale / zero; 132 tokens per sequence read as 1152 B bf16 rows; one 4 B page id per
+    64 tokens; per head the bf16 query (1152 B) and output (1024 B) and the fp32 lse; two flops per
+    multiply-add over 576 score and 512 output channels."""
+    b = _bench_module()
+    assert b.kv_bytes_per_token(4) == 324 and b.kv_bytes_per_token(2) == 196
+    per_seq = 324 * (131072 - 132) + 1152 * 132 + 4 * 2048 + 128 * (1152 + 1024 + 4)
+    assert per_seq == 42_863_856
+    by, fl = b.algorithmic([131072] * 8, 128, 4)
+    assert by == 8 * per_seq == 342_910_848
+    assert fl == 8 * 2 * 128 * (576 + 512) * 131072 == 292_057_776_128
+    # short sequences are read from bf16 only
+    by_s, fl_s = b.algorithmic([100], 16, 2)
+    assert by_s == 1152 * 100 + 4 * 2 + 16 * 2180 and fl_s == 2 * 16 * 1088 * 100
