@@ -202,10 +202,11 @@ def test_absorbed_equals_explicit_heads():
 
 
 # ----------------------------------------------------------------- P5: q = 0 closed form + selection
+@pytest.mark.parametrize("bits_c", [4, 2])
 @pytest.mark.parametrize("n", [1, 4, 5, 131, 132, 133, 700])
-def test_zero_query_uniform_and_selection(n):
-    """q = 0: output = mean of the selected rows, lse = ln N; selected rows follow the window rule."""
-    bits_c = 4
+def test_zero_query_uniform_and_selection(n, bits_c):
+    """q = 0: output = mean of the selected rows, lse = ln N; selected rows follow the window rule,
+    and every packed token equals its copy decoded straight from the page bytes (4- and 2-bit)."""
     rows = mi.rows(13, 0, n)
     cc, cr, meta = oracle.quantize(rows, bits_c)
     npages = (n + 63) // 64
@@ -230,9 +231,9 @@ def test_empty_sequence():
 
 
 # ----------------------------------------------------------------- P6: brute force on tiny contexts
-def test_brute_force_tiny_contexts():
+@pytest.mark.parametrize("bits_c", [4, 2])
+def test_brute_force_tiny_contexts(bits_c):
     """N in 1..200 and 255..257: oracle == explicit-loop attention over page-decoded tokens."""
-    bits_c = 4
     rows_all = mi.rows(14, 0, 257)
     q = mi.queries(14, 1, 2)[0]
     cc, cr, meta = oracle.quantize(rows_all, bits_c)
@@ -287,3 +288,55 @@ def test_identical_tokens_closed_form():
         ref = (n_bf * math.exp(s_raw - m) * raw[:512] + (n - n_bf) * math.exp(s_deq - m) * deq[:512]) / l
         np.testing.assert_allclose(out[h], ref, rtol=1e-11, atol=1e-11)
         assert abs(lse[h] - (m + math.log(l))) < 1e-11
+
+
+# ----------------------------------------------------------------- O4: sink and recent-ring contents
+# The writer keeps the bf16 rows of the first n_sink tokens and of the most recent n_recent tokens
+# (onedev.kr review, "How it is used"), the ring row of position p being p mod n_recent.  The maps
+# below were worked out by hand for each (N, n_recent) and are written as segments
+# (first ring row, last ring row, position held by the first row); a segment's rows hold
+# consecutive positions.
+RING_MAPS = {
+    (1, 1): [(0, 0, 0)],
+    (4, 1): [(0, 0, 3)],
+    (5, 1): [(0, 0, 4)],
+    (131, 1): [(0, 0, 130)],
+    (132, 1): [(0, 0, 131)],
+    (133, 1): [(0, 0, 132)],
+    (300, 1): [(0, 0, 299)],
+    (1, 3): [(0, 0, 0)],
+    (4, 3): [(0, 0, 3), (1, 2, 1)],                    # positions 1, 2, 3
+    (5, 3): [(0, 1, 3), (2, 2, 2)],                    # positions 2, 3, 4
+    (131, 3): [(0, 1, 129), (2, 2, 128)],              # positions 128, 129, 130
+    (132, 3): [(0, 2, 129)],                           # positions 129, 130, 131
+    (133, 3): [(0, 0, 132), (1, 2, 130)],              # positions 130, 131, 132
+    (300, 3): [(0, 2, 297)],                           # positions 297, 298, 299
+    (1, 128): [(0, 0, 0)],
+    (4, 128): [(0, 3, 0)],
+    (5, 128): [(0, 4, 0)],
+    (131, 128): [(0, 2, 128), (3, 127, 3)],            # positions 3 .. 130, wrapped after 127
+    (132, 128): [(0, 3, 128), (4, 127, 4)],            # positions 4 .. 131
+    (133, 128): [(0, 4, 128), (5, 127, 5)],            # positions 5 .. 132
+    (300, 128): [(0, 43, 256), (44, 127, 172)],        # positions 172 .. 299, wrapped after 255
+}
+SINK_MAPS = {1: [0], 4: [0, 1, 2, 3], 5: [0, 1, 2, 3], 131: [0, 1, 2, 3], 132: [0, 1, 2, 3],
+             133: [0, 1, 2, 3], 300: [0, 1, 2, 3]}
+
+
+@pytest.mark.parametrize("n,n_recent", sorted(RING_MAPS))
+def test_bf16_buffers_hand_maps(n, n_recent):
+    """The oracle's expected sink and ring rows (the reference for every writer byte test) equal
+    the hand-written maps above: which positions are kept, and in which ring row each one sits."""
+    rows = np.zeros((n, 576), np.uint16)
+    rows[:, 0] = np.arange(n)                 # a row's position, readable from its first channel
+    rows[:, 1] = 0x4000 + np.arange(n) % 7    # and some other content
+    sink, ring = oracle.bf16_buffers(rows, n_sink=4, n_recent=n_recent)
+    expect = {}
+    for lo, hi, p0 in RING_MAPS[(n, n_recent)]:
+        for k, slot in enumerate(range(lo, hi + 1)):
+            expect[slot] = p0 + k
+    assert {s: int(r[0]) for s, r in ring.items()} == expect
+    for s, r in ring.items():
+        assert np.array_equal(r, rows[expect[s]])
+    assert {i: int(r[0]) for i, r in sink.items()} == {i: i for i in SINK_MAPS[n]}
+    assert oracle.bf16_buffers(rows, n_sink=0, n_recent=n_recent)[0] == {}
