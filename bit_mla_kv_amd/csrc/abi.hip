@@ -1,10 +1,17 @@
 // Host side of the C ABI declared in include/mla_lowbit.h: argument checks,
 // status strings, the thread-local error message and the kernel launches.
-// Nothing here allocates device memory or synchronises the stream.
+// Nothing here allocates device memory.  Only the validation mode
+// (MLA_LOWBIT_VALIDATE=1) synchronises the stream and copies index data and
+// the decode counters to the host.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
 
 #include "../../include/mla_lowbit.h"
 #include "mla_internal.h"
@@ -67,6 +74,119 @@ int device_status(hipError_t e, const char* what) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ---------------------------------------------------------------- validation mode
+bool validate_mode() {
+  const char* e = getenv("MLA_LOWBIT_VALIDATE");
+  return e && e[0] && strcmp(e, "0") != 0;
+}
+
+int spin_limit() {
+  const char* e = getenv("MLA_LOWBIT_SPIN_LIMIT");  // test knob: bound of a handshake wait
+  if (!e || !e[0]) return mla::kDefaultSpin;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (int)std::min<long>(v, mla::kDefaultSpin);
+}
+
+template <typename T>
+hipError_t fetch(std::vector<T>& v, const void* dptr, size_t n) {
+  v.resize(n);
+  if (n == 0) return hipSuccess;
+  return hipMemcpy(v.data(), dptr, n * sizeof(T), hipMemcpyDeviceToHost);
+}
+
+// The slot's pages [first, last] must be inside its table row and name pages of the pool, and no
+// physical page may serve two slots.
+int check_pages(const mla_lowbit_cache* c, const std::vector<int32_t>& bt, int slot, int64_t first, int64_t last,
+                std::unordered_map<int32_t, int>& owner, const char* what) {
+  for (int64_t i = first; i <= last; ++i) {
+    if (i >= c->max_pages_per_seq)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: %s: slot %d needs page index %lld, max_pages_per_seq is %d",
+                  what, slot, (long long)i, c->max_pages_per_seq);
+    const int32_t pg = bt[(size_t)slot * c->max_pages_per_seq + i];
+    if (pg < 0 || pg >= c->num_pages)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: %s: block_table[%d][%lld] = %d outside [0, %lld)", what, slot,
+                  (long long)i, pg, (long long)c->num_pages);
+    auto it = owner.emplace(pg, slot).first;
+    if (it->second != slot)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: %s: page %d is in the tables of slots %d and %d", what, pg,
+                  it->second, slot);
+  }
+  return MLA_LOWBIT_OK;
+}
+
+// Device-resident arguments of a decode: slots and lengths in range, and the pages every sequence
+// reads from packed copies valid and unshared.
+int validate_decode_inputs(const mla_lowbit_cache* c, const int32_t* seq_slot, const int32_t* seq_len, int batch,
+                           int max_seq_len, hipStream_t s) {
+  int st = device_status(hipStreamSynchronize(s), "validate: stream synchronize");
+  if (st != MLA_LOWBIT_OK) return st;
+  std::vector<int32_t> slots, lens, bt;
+  if ((st = device_status(fetch(slots, seq_slot, batch), "validate: copy seq_slot")) != MLA_LOWBIT_OK) return st;
+  if ((st = device_status(fetch(lens, seq_len, batch), "validate: copy seq_len")) != MLA_LOWBIT_OK) return st;
+  if ((st = device_status(fetch(bt, c->block_table, (size_t)c->num_slots * c->max_pages_per_seq),
+                          "validate: copy block_table")) != MLA_LOWBIT_OK)
+    return st;
+  std::unordered_map<int32_t, int> owner;
+  for (int b = 0; b < batch; ++b) {
+    if (slots[b] < 0 || slots[b] >= c->num_slots)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: seq_slot[%d] = %d outside [0, %d)", b, slots[b], c->num_slots);
+    if (lens[b] < 0 || lens[b] > max_seq_len)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: seq_len[%d] = %d outside [0, max_seq_len = %d]", b, lens[b],
+                  max_seq_len);
+    const int64_t lo = c->layout.n_sink, hi = (int64_t)lens[b] - c->layout.n_recent;  // packed tokens [lo, hi)
+    if (hi > lo && (st = check_pages(c, bt, slots[b], lo / mla::kPageTokens, (hi - 1) / mla::kPageTokens, owner,
+                                     "decode")) != MLA_LOWBIT_OK)
+      return st;
+  }
+  return MLA_LOWBIT_OK;
+}
+
+// Device-resident arguments of an append: slots, positions and lengths consistent, (slot, pos)
+// pairs distinct, and every written page valid and unshared.
+int validate_append_inputs(const mla_lowbit_cache* c, const int32_t* token_slot, const int32_t* token_pos,
+                           const int32_t* slot_len_after, int n, hipStream_t s) {
+  int st = device_status(hipStreamSynchronize(s), "validate: stream synchronize");
+  if (st != MLA_LOWBIT_OK) return st;
+  std::vector<int32_t> slots, pos, after, bt;
+  if ((st = device_status(fetch(slots, token_slot, n), "validate: copy token_slot")) != MLA_LOWBIT_OK) return st;
+  if ((st = device_status(fetch(pos, token_pos, n), "validate: copy token_pos")) != MLA_LOWBIT_OK) return st;
+  if ((st = device_status(fetch(after, slot_len_after, c->num_slots), "validate: copy slot_len_after")) != MLA_LOWBIT_OK)
+    return st;
+  if ((st = device_status(fetch(bt, c->block_table, (size_t)c->num_slots * c->max_pages_per_seq),
+                          "validate: copy block_table")) != MLA_LOWBIT_OK)
+    return st;
+  std::unordered_set<int64_t> seen;
+  std::unordered_map<int32_t, int> owner;
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= c->num_slots)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: token_slot[%d] = %d outside [0, %d)", i, slots[i], c->num_slots);
+    if (pos[i] < 0 || pos[i] >= after[slots[i]])
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: token_pos[%d] = %d outside [0, slot_len_after[%d] = %d)", i,
+                  pos[i], slots[i], after[slots[i]]);
+    if (!seen.insert(((int64_t)slots[i] << 32) | (uint32_t)pos[i]).second)
+      return fail(MLA_LOWBIT_ERR_INVALID_ARG, "validate: (slot %d, pos %d) appears twice", slots[i], pos[i]);
+    const int64_t pi = pos[i] / mla::kPageTokens;
+    if ((st = check_pages(c, bt, slots[i], pi, pi, owner, "append")) != MLA_LOWBIT_OK) return st;
+  }
+  return MLA_LOWBIT_OK;
+}
+
+// After a decode in validation mode: the counters the kernels left in the workspace header.
+int check_decode_counters(const int32_t* hdr_dev, hipStream_t s) {
+  int st = device_status(hipStreamSynchronize(s), "validate: stream synchronize");
+  if (st != MLA_LOWBIT_OK) return st;
+  int32_t h[8];
+  if ((st = device_status(hipMemcpy(h, hdr_dev, sizeof(h), hipMemcpyDeviceToHost), "validate: copy counters")) !=
+      MLA_LOWBIT_OK)
+    return st;
+  if (h[mla::kHdrGiveUps] || h[mla::kHdrBadPages] || h[mla::kHdrBadSeqs] || h[mla::kHdrDropped])
+    return fail(MLA_LOWBIT_ERR_DEVICE,
+                "validate: decode results are unreliable: %d handshake wait(s) gave up, %d page read(s) with a "
+                "block-table entry out of range, %d sequence(s) with a bad slot or length, %d work item(s) dropped",
+                h[mla::kHdrGiveUps], h[mla::kHdrBadPages], h[mla::kHdrBadSeqs], h[mla::kHdrDropped]);
+  return MLA_LOWBIT_OK;
+}
+
 struct WsLayout {
   size_t hdr_off, items_off, seq_off, ml_off, z_off, o_off, total;
 };
@@ -120,7 +240,11 @@ int mla_lowbit_quantize_append(const mla_lowbit_cache* cache, const void* kv_new
   p.token_pos = token_pos;
   p.slot_len_after = slot_len_after;
   p.n_tokens = n_tokens;
-  return device_status(mla::launch_append(p, static_cast<hipStream_t>(stream)), "quantize_append launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_mode() &&
+      (st = validate_append_inputs(cache, token_slot, token_pos, slot_len_after, n_tokens, s)) != MLA_LOWBIT_OK)
+    return st;
+  return device_status(mla::launch_append(p, s), "quantize_append launch");
 }
 
 size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_t batch, int32_t num_heads,
@@ -185,6 +309,8 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.seq_len = seq_len;
   p.batch = batch;
   p.heads = num_heads;
+  p.max_seq_len = max_seq_len;
+  p.spin_limit = spin_limit();
   p.q_len = q_len;
   p.heads_per_query = heads_per_query;
   p.scale_log2e = (float)((double)softmax_scale * 1.4426950408889634);
@@ -204,13 +330,21 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool validate = validate_mode();
+  if (validate && (st = validate_decode_inputs(cache, seq_slot, seq_len, batch, max_seq_len, s)) != MLA_LOWBIT_OK)
+    return st;
+  // everything a launch of this call can be refused for is checked before the first one
+  if ((st = device_status(mla::prepare_decode(p, cache->layout.bits_c), "decode kernel setup")) != MLA_LOWBIT_OK)
+    return st;
   st = device_status(mla::launch_plan(p, s), "plan launch");
   if (st != MLA_LOWBIT_OK) return st;
   if (ev0 && (st = device_status(hipEventRecord(ev0, s), "profile start event")) != MLA_LOWBIT_OK) return st;
   st = device_status(mla::launch_decode(p, cache->layout.bits_c, s), "decode launch");
   if (st != MLA_LOWBIT_OK) return st;
   if (ev1 && (st = device_status(hipEventRecord(ev1, s), "profile stop event")) != MLA_LOWBIT_OK) return st;
-  return device_status(mla::launch_combine(p, s), "combine launch");
+  st = device_status(mla::launch_combine(p, s), "combine launch");
+  if (st != MLA_LOWBIT_OK || !validate) return st;
+  return check_decode_counters(p.plan_hdr, s);
 }
 
 int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,

@@ -132,8 +132,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   if (p.n_tokens <= 0) return hipSuccess;
   const int blocks = (p.n_tokens + 3) / 4;
-  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  AppendParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(append_kernel), dim3(blocks), dim3(256), args, 0, stream);
 }
 
 }  // namespace mla

@@ -65,6 +65,15 @@ bool decode_config(int heads, int n_sink, int n_recent, int batch, int max_seq_l
   return true;
 }
 
+hipError_t prepare_decode(const DecodeParams& p, int bits_c) {
+  const int hpw = p.heads / p.head_groups;
+  const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (hpw == 64) return prepare_decode64(p, bits_c);
+  if (hpw == 16) return (bits_c == 4 || bits_c == 2) ? hipSuccess : hipErrorInvalidValue;
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream) {
   const int hpw = p.heads / p.head_groups;
   if (hpw == 64) return launch_decode64(p, bits_c, stream);

@@ -29,7 +29,7 @@
 // publishes block t once its buffer is written, and writes block t only after
 // the PV wave has released block t - 2 (two buffers), so it runs up to a block
 // ahead.  Every wait is bounded, so a broken handshake gives wrong values,
-// never a hang.  The four pairs' partials are merged through LDS at the end;
+// never a hang; a wait that gives up is counted in the workspace header.  The four pairs' partials are merged through LDS at the end;
 // the split's partial stays unnormalised with its running max and sum for the
 // combine.
 #include <algorithm>
@@ -48,7 +48,6 @@ constexpr int kAhead = 3;             // blocks a QK wave holds in registers (bl
 constexpr int kSV = 528;              // V tile row stride (halves): conflict-free b128 row writes and transposed reads
 constexpr int kPS = 16;               // probability / zero row stride (halves), rows are tokens
 constexpr float kRescale = 8.0f;      // lazy max refresh threshold, log2 units
-constexpr int kSpin = 1 << 18;        // bound of a handshake wait (polls)
 
 template <int BITS_C>
 struct Geo {
@@ -66,8 +65,9 @@ struct __align__(16) PairTiles {
   f16 Z[kB][kPS];     // fp16 zeros [token][z_0..z_7, z_8, 0 x 7]
   f16 SV[8][kB];      // fp16 PV group scales [group][token]
   float alpha[16];    // per-head factor for the PV accumulators before this block (running max refreshed)
-  int resc;           // 1: apply alpha before this block
-  int pad[3];
+  int resc;           // bit 0: apply alpha before this block; bit 1: the PV scale exponent changed
+  int pv_exp;         // E: the block's PV scales are fp16(s * 2^-E) (valid when bit 1 of resc is set)
+  int pad[2];
 };
 union __align__(16) Tiles16 {
   PairTiles pt[kPairs][2];
@@ -99,11 +99,13 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 // Handshake flags live in an LDS object of their own, read and written as volatile words.
 typedef __attribute__((address_space(3))) volatile int lds_vint;
-__device__ __forceinline__ void wait_at_least(lds_vint* flag, int target) {
-  for (int i = 0; i < kSpin; ++i) {
-    if (__builtin_amdgcn_readfirstlane(*flag) >= target) return;
+// Returns 1 when the wait gave up after `spin` polls (counted into the workspace header).
+__device__ __forceinline__ int wait_at_least(lds_vint* flag, int target, int spin) {
+  for (int i = 0; i < spin; ++i) {
+    if (__builtin_amdgcn_readfirstlane(*flag) >= target) return 0;
     __builtin_amdgcn_s_sleep(1);
   }
+  return 1;
 }
 // publish a flag value once this wave's earlier LDS writes have completed
 __device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int hg = kx % p.head_groups;
   const int item = xcd + 8 * (kx / p.head_groups);
-  if (item >= min(p.plan_hdr[0], p.max_items)) return;
+  if (item >= min(p.plan_hdr[kHdrItems], p.max_items)) return;
   const int4 itm = reinterpret_cast<const int4*>(p.items)[item];
   const int b = itm.x;
   const bool packed = itm.w == 0;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   constexpr int kPT = (int)sizeof(PairTiles);
   constexpr int oP = (int)offsetof(PairTiles, P), oZ = (int)offsetof(PairTiles, Z);
   constexpr int oSV = (int)offsetof(PairTiles, SV), oA = (int)offsetof(PairTiles, alpha);
-  constexpr int oR = (int)offsetof(PairTiles, resc);
+  constexpr int oR = (int)offsetof(PairTiles, resc), oE = (int)offsetof(PairTiles, pv_exp);
   const int pb0 = pr * 2 * kPT;  // the pair's first buffer
   const int rsel = 4 * G + (L16 >> 2), csel = 4 * (L16 & 3);
   const int o_vtr = pb0 + 2 * (rsel * kSV + csel);       // V^T operand, + 32 per 16 channel positions
@@ -179,9 +181,12 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
   const int o_svw = pb0 + oSV + 2 * L16;
   const int o_al = pb0 + oA;
   const int o_rs = pb0 + oR;
+  const int o_pe = pb0 + oE;
   __syncthreads();  // flags initialised
 
   auto& mg = s_tiles.mg;
+  const int spin = p.spin_limit;
+  int give_ups = 0, bad_pages = 0;  // (uniform across the wave)
   if (w < kPairs) {
     // ============================== QK wave of pair pr ==============================
     const int row = 16 * pr + L16;  // the lane's token row within a page
@@ -232,6 +237,25 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       m_run[i] = -__builtin_inff();
       l_part[i] = 0.f;
     }
+    // PV scale normaliser of a packed item: its PV scales go to the tile as fp16(s * 2^-pv_e), with
+    // pv_e raised (never lowered) so that the largest scale seen so far sits in [2^5, 2^6); with
+    // probabilities <= 2^8 (lazy max refresh) every product p * s * 2^-pv_e stays below 2^14.
+    int pv_e = 0, ebit = 0;                 // ebit: 2 when the current block raised pv_e
+    float pv_inv = 1.f, pv_hi = 0x1p-126f;  // 2^-pv_e; raise when a scale reaches pv_hi = 2^(pv_e + 6)
+    // smax: the larger of the two PV scales this lane writes (groups 2G, 2G + 1 of token L16), so
+    // the maximum over the wave is the block's largest scale
+    auto pv_scale_check = [&](float smax) {
+      ebit = 0;
+      if (__builtin_amdgcn_ballot_w64(smax >= pv_hi) == 0) return;
+      float m = smax;  // (some lane holds a scale >= pv_hi >= 2^-126: the maximum is a normal number)
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+      const int bits = __builtin_amdgcn_readfirstlane(__float_as_int(m));
+      pv_e = min(max(((bits >> 23) & 0xFF) - 127 - 5, -100), 120);
+      pv_inv = __builtin_ldexpf(1.f, -pv_e);
+      pv_hi = __builtin_ldexpf(1.f, pv_e + 6);
+      ebit = 2;
+    };
     auto needs_refresh = [&](f32x4 S) {
       bool need = false;
 #pragma unroll
@@ -251,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       if (L16 == 0) *reinterpret_cast<lds_ptr<f32x4>>(tb + (o_al + so + 16 * G)) = alpha;
     };
     // softmax of block t with the current running maxima, probabilities to the P tile, publish
-    auto publish = [&](f32x4 S, int t, bool resc, int so) {
+    auto publish = [&](f32x4 S, int t, int rbits, int so) {
       f16x4 pz;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -261,7 +285,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         pz[i] = (f16)e;
       }
       *reinterpret_cast<lds_ptr<f16x4>>(tb + (o_pwr + so)) = pz;
-      if (lane == 0) *reinterpret_cast<lds_ptr<int>>(tb + (o_rs + so)) = resc ? 1 : 0;
+      if (lane == 0) {
+        *reinterpret_cast<lds_ptr<int>>(tb + (o_rs + so)) = rbits;
+        if (rbits & 2) *reinterpret_cast<lds_ptr<int>>(tb + (o_pe + so)) = pv_e;
+      }
       signal(fl + 0, t, lane);
     };
     // the QK of one block from K-step words kw(g) (C4 / RoPE: two dwords, C2: one), its scales and
@@ -307,8 +334,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         const uint32_t a0 = (G & 1) ? mw[2] : mw[0], b0 = (G & 1) ? mw[6] : mw[4];
         const uint32_t a1 = (G & 1) ? mw[3] : mw[1], b1 = (G & 1) ? mw[7] : mw[5];
         const uint32_t m0 = (G & 2) ? b0 : a0, m1 = (G & 2) ? b1 : a1;
-        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G)) = (f16)bf16f(m0 & 0xFFFFu);
-        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G + 32)) = (f16)bf16f(m1 & 0xFFFFu);
+        const float s0 = bf16f(m0 & 0xFFFFu), s1 = bf16f(m1 & 0xFFFFu);
+        if (codes) pv_scale_check(fmaxf(s0, s1));  // (bf16 items keep pv_inv = 1)
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G)) = (f16)(s0 * pv_inv);
+        *reinterpret_cast<lds_ptr<f16>>(tb + (o_svw + so + 64 * G + 32)) = (f16)(s1 * pv_inv);
         if (G == 0) {
           *reinterpret_cast<lds_ptr<f16x8>>(tb + (o_zwr + so)) = zlo;
           *reinterpret_cast<lds_ptr<f16>>(tb + (o_zwr + so + 16)) = z8;
@@ -331,7 +360,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
       };
       auto load = [&](int t, BlockRegs& R) {
         int pg = bt[min(t, last)];
-        if (pg < 0 || pg >= p.num_pages) pg = 0;  // contract violation: wrong values, no fault
+        if (pg < 0 || pg >= p.num_pages) {  // contract violation: wrong values, no fault; counted
+          pg = 0;
+          ++bad_pages;
+        }
         const uint8_t* base = p.pages + (int64_t)pg * GE::PB;
         const uint8_t* crow = base + row * GE::CB + (BITS_C == 4 ? 8 : 4) * G;
 #pragma unroll
@@ -354,11 +386,11 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
           auto kw = [&](int g) -> u32x2 { return R.kv[g]; };
           auto none = [&](int, int) { return f16x8{}; };
           const int so = (t & 1) * kPT;
-          wait_at_least(fl + 1, t - 2);  // the PV wave has read buffer t % 2 (block t - 2)
+          give_ups += wait_at_least(fl + 1, t - 2, spin);  // the PV wave has read buffer t % 2 (block t - 2)
           const f32x4 S = block_qk(kw, none, mw, valid, true, so);
           const bool resc = needs_refresh(S);
           if (resc) refresh(S, so);
-          publish(S, t, resc, so);
+          publish(S, t, (resc ? 1 : 0) | ebit, so);
         }
         load(t + kAhead, R);  // the registers of block t now take block t + 3
       };
@@ -401,13 +433,15 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         };
         auto none = [&](int) { return u32x2{0u, 0u}; };
         const int so = (t & 1) * kPT;
-        wait_at_least(fl + 1, t - 2);  // buffer t % 2 is free
+        give_ups += wait_at_least(fl + 1, t - 2, spin);  // buffer t % 2 is free
         const f32x4 S = block_qk(none, kf16, mw, valid, false, so);
         const bool resc = needs_refresh(S);
         if (resc) refresh(S, so);
-        publish(S, t, resc, so);
+        publish(S, t, resc ? 1 : 0, so);
       }
     }
+    if (lane == 0 && give_ups) atomicAdd(p.plan_hdr + kHdrGiveUps, give_ups);
+    if (lane == 0 && bad_pages) atomicAdd(p.plan_hdr + kHdrBadPages, bad_pages);
     // ---- merge: this pair's running max and sum
     __syncthreads();  // every wave is done with its tiles; the merge area overlays them
 #pragma unroll
@@ -428,8 +462,9 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) O[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 oz = {0.f, 0.f, 0.f, 0.f};  // rows z index 4G + i
+    int cur_e = 0;                     // O holds sum_t code * p * s * 2^-cur_e (packed items)
     for (int t = 0; t < n_blocks; ++t) {
-      wait_at_least(fl + 0, t);  // block t published
+      give_ups += wait_at_least(fl + 0, t, spin);  // block t published
       // block t's operands into registers (k = tokens 4G .. 4G + 3), then release its buffer
       const int so = (t & 1) * kPT;
       const f16x4 pb = lds_tr4((lds_ptr<f16>)(tb + (o_ptr + so)));  // B: head L16
@@ -440,12 +475,19 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) va[cb] = lds_tr4((lds_ptr<f16>)(tb + (o_vtr + so + 32 * cb)));
       const int resc = __builtin_amdgcn_readfirstlane(lds_load<int>(tb + (o_rs + so)));
+      const int new_e = __builtin_amdgcn_readfirstlane(lds_load<int>(tb + (o_pe + so)));
       const float alpha = lds_load<float>(tb + (o_al + so + 4 * L16));
       signal(fl + 1, t, lane);
       if (resc) {
+        const float a = (resc & 1) ? alpha : 1.f;
+        float ae = a;
+        if (resc & 2) {  // the PV scales now carry 2^-new_e: bring the sums to that scale
+          ae = a * __builtin_ldexpf(1.f, cur_e - new_e);
+          cur_e = new_e;
+        }
 #pragma unroll
-        for (int cb = 0; cb < 32; ++cb) O[cb] *= alpha;
-        oz *= alpha;
+        for (int cb = 0; cb < 32; ++cb) O[cb] *= ae;
+        oz *= a;
       }
       oz = mfma16k(za, pb, oz);
 #pragma unroll
@@ -455,6 +497,7 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
         for (int c = 0; c < 4; ++c) O[4 * g + c] = mfma16k(va[4 * g + c], bop, O[4 * g + c]);
       }
     }
+    if (lane == 0 && give_ups) atomicAdd(p.plan_hdr + kHdrGiveUps, give_ups);
     // ---- merge the four pairs' partials (per head: max-shifted sums) and write the split's row
     __syncthreads();  // every wave is done with its tiles; the merge area overlays them
     __syncthreads();  // the QK waves' running maxima and sums are in place
@@ -464,8 +507,9 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
     {
       const float mw = mg.m[pr][L16];
       const float f = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      const float fe = f * __builtin_ldexpf(1.f, cur_e);  // undo the PV scale normaliser
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) O[cb] *= f;
+      for (int cb = 0; cb < 32; ++cb) O[cb] *= fe;
       oz *= f;
     }
     if (G < 2) {
@@ -535,8 +579,10 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
 template <int BITS_C>
 hipError_t launch16(const DecodeParams& p, hipStream_t stream) {
   const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
-  hipLaunchKernelGGL(decode16_kernel<BITS_C>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(decode16_kernel<BITS_C>), dim3((unsigned)blocks),
+                         dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace

@@ -79,11 +79,15 @@ struct PVRegs {
 };
 
 // Page id of page_idx of the slot's block table, read through the constant address space (scalar
-// loads); an index or id outside the table or the pool reads page 0 (wrong values, no fault).
+// loads); an index or id outside the table or the pool reads page 0 (wrong values, no fault) and
+// is counted in *bad (uniform across the wave).
 typedef __attribute__((address_space(4))) const int32_t cint;
-__device__ __forceinline__ int64_t page_of(const DecodeParams& p, cint* bt, int page_idx) {
-  int64_t pg = (page_idx < p.max_pages) ? (int64_t)bt[min(page_idx, p.max_pages - 1)] : 0;
-  if (pg < 0 || pg >= p.num_pages) pg = 0;
+__device__ __forceinline__ int64_t page_of(const DecodeParams& p, cint* bt, int page_idx, int* bad) {
+  int64_t pg = (page_idx < p.max_pages) ? (int64_t)bt[min(page_idx, p.max_pages - 1)] : -1;
+  if (pg < 0 || pg >= p.num_pages) {
+    pg = 0;
+    ++*bad;
+  }
   return pg;
 }
 
@@ -113,9 +117,11 @@ struct __align__(16) Smem64 {
   f16 probT[2][kT][kPT];           // fp16 probabilities [token][head] of steps k (QK) and k - 1 (PV)
   float sq[kSlots][kGroups][kT];   // s_g * scale * log2 e at sq_pos(token); 0 for masked tokens
   float bias[kSlots][kT];          // at sq_pos(token): 0 valid, -inf masked
-  f16 svh[kSlots][8][kT];          // PV group scale s_g (fp16); 0 for masked tokens
+  f16 svh[kSlots][8][kT];          // PV group scale s_g * 2^-E_g (fp16); 0 for masked tokens
   float alpha[2][kHW];             // per-head rescale factor for the PV accumulators
-  int resc[2][4];                  // per-QK-wave "some head was rescaled" flags
+  int resc[2][4];                  // per-QK-wave flags: bit 0 some head was rescaled, bit 1 the wave's
+                                   // groups changed their PV scale exponent
+  int pve[kSlots][8];              // PV scale exponent E_g of a tile: svh holds fp16(s_g * 2^-E_g)
 };
 
 // Per-token QK constants sit so that one 8-byte read gives a lane the values of its token in
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int hg = kx % p.head_groups;
   const int item = xcd + 8 * (kx / p.head_groups);
-  if (item >= min(p.plan_hdr[0], p.max_items)) return;
+  if (item >= min(p.plan_hdr[kHdrItems], p.max_items)) return;
   const int4 itm = reinterpret_cast<const int4*>(p.items)[item];
   const int b = itm.x;
   const bool packed = itm.w == 0;  // otherwise the item holds the sequence's bf16 tokens
@@ -235,12 +241,13 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     // ====== QK + unpack waves: QK of heads head0 + 16w + L16, unpacking of a quarter of each tile ======
     const int ft = tid;  // 0 .. 255
     cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
+    int bad_pages = 0;
     // packed bytes of tile min(t, n_tiles - 1) (half t % 2 of page page0 + t / 2) into registers;
     // every call issues the same loads, so the compiler's load counting stays exact
     auto load = [&](int t, TileRegs<BITS_C>& R) {
       t = min(t, n_tiles - 1);
       const int hs = t & 1;
-      const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1)) * (int64_t)GE::PB;
+      const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1), &bad_pages) * (int64_t)GE::PB;
       const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + hs * kT * GE::CB);
       const uint32_t* srcR = reinterpret_cast<const uint32_t*>(base + GE::ROPE0 + hs * kT * kDr / 2);
       const uint32_t* srcM = reinterpret_cast<const uint32_t*>(base + GE::META0 + hs * kT * 4 * kGroups);
@@ -250,6 +257,12 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       R.m[0] = srcM[(ft & 31) * kGroups + (ft >> 5)];
       R.m[1] = srcM[(ft & 31) * kGroups + 8];
     };
+    // PV scale normaliser of a packed item, per group (this thread's group ft / 32: lanes 0..31 of
+    // wave w hold group 2w, lanes 32..63 group 2w + 1): the tile gets fp16(s * 2^-pv_e), pv_e raised
+    // (never lowered) so that the largest scale seen so far sits in [2^5, 2^6); with probabilities
+    // <= 2^8 (lazy max refresh) every PV product p * s * 2^-pv_e stays below 2^14.
+    int pv_e = 0, echg = 0;
+    float pv_inv = 1.f, pv_hi = 0x1p-126f;  // 2^-pv_e; raise when a scale reaches pv_hi = 2^(pv_e + 6)
     // unpack tile t into ring slot t % 3
     auto fill = [&](int t, const TileRegs<BITS_C>& R) {
       const int sl = t % kSlots;
@@ -280,8 +293,22 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       {
         const int g = ft >> 5;
         const float sc = valid ? bf16f(R.m[0] & 0xFFFFu) : 0.f;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(sc >= pv_hi);
+        echg = 0;
+        if (hit) {  // rare: some scale of the tile reached 2^(pv_e + 6) (or the first nonzero scale)
+          float hm = sc;  // maximum over the half wave (the group's 32 tokens)
+#pragma unroll
+          for (int d = 1; d < 32; d <<= 1) hm = fmaxf(hm, __shfl_xor(hm, d, 64));
+          if (hm >= pv_hi) {  // (a normal number: pv_hi >= 2^-126)
+            pv_e = min(max(((__float_as_int(hm) >> 23) & 0xFF) - 127 - 5, -100), 120);
+            pv_inv = __builtin_ldexpf(1.f, -pv_e);
+            pv_hi = __builtin_ldexpf(1.f, pv_e + 6);
+          }
+          if (r == 0) sm.pve[sl][g] = pv_e;
+          echg = 2;
+        }
         sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
-        sm.svh[sl][g][r] = (f16)sc;
+        sm.svh[sl][g][r] = (f16)(sc * pv_inv);
         tile[r * kS + kZ + g] = (f16)(valid ? bf16f(R.m[0] >> 16) : 0.f);
         if (g == 0) sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
       }
@@ -427,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       *reinterpret_cast<f16x4*>(prow) = pz[0];
       *reinterpret_cast<f16x4*>(prow + 16 * kPT) = pz[1];
       if (L16 == 0) *reinterpret_cast<f32x4*>(&sm.alpha[pb][hc]) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
-      if (lane == 0) sm.resc[pb][w] = any ? 1 : 0;
+      if (lane == 0) sm.resc[pb][w] = (any ? 1 : 0) | echg;  // echg: set by the fill of tile k
     };
 
     if (packed) {
@@ -452,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         step(k + 2, R2, R0);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no loads left in flight at exit
+      if (bad_pages && lane == 0) atomicAdd(p.plan_hdr + kHdrBadPages, bad_pages);
     } else {
       const TileRegs<BITS_C> none{};
       BfRegs X;
@@ -488,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     const int v = w - 4;
     f32x4 oz = {0.f, 0.f, 0.f, 0.f};  // rows z index 4G + i, column head 16v + L16: sum_t p z
     f32x16 O[2][4];                    // [head block][channel block]
+    int cur_e[2] = {0, 0};             // O[.][2 gi + c] holds sum_t code * p * s * 2^-cur_e[gi]
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -521,11 +550,20 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         }
         // the refresh flags are read with the operands, so one wait covers both
         if (rf[0] | rf[1] | rf[2] | rf[3]) {
+          float ef[2] = {1.f, 1.f};
+          if (rf[v] & 2) {  // this wave's groups 2v, 2v + 1 changed their PV scale exponent
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+              const int ne = sm.pve[sl][2 * v + gi];
+              ef[gi] = __builtin_ldexpf(1.f, cur_e[gi] - ne);
+              cur_e[gi] = ne;
+            }
+          }
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             const float a = sm.alpha[pb][32 * hb + l32];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) O[hb][cb] *= a;
+            for (int cb = 0; cb < 4; ++cb) O[hb][cb] *= a * ef[cb >> 1];
           }
           oz *= sm.alpha[pb][16 * v + L16];
         }
@@ -555,7 +593,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
       auto pload = [&](int t, PVRegs<BITS_C>& R) {
         t = min(t, n_tiles - 1);
-        const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1)) * (int64_t)GE::PB;
+        int uncounted = 0;  // (the QK waves count the same reads)
+        const uint8_t* base = p.pages + page_of(p, bt, page0 + (t >> 1), &uncounted) * (int64_t)GE::PB;
         const uint32_t* srcC = reinterpret_cast<const uint32_t*>(base + (t & 1) * kT * GE::CB);
 #pragma unroll
         for (int i = 0; i < GE::CPT - GE::CQ; ++i) R.c[i] = srcC[pt + 256 * (GE::CQ + i)];
@@ -601,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     // lane takes two values from the other, so that the lower half holds channels 0..3 and the
     // upper half channels 4..7, written as one 16-byte store.
     const bool odd = half;
+    const float e2[2] = {__builtin_ldexpf(1.f, cur_e[0]), __builtin_ldexpf(1.f, cur_e[1])};  // undo 2^-E_g
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float* dh = p.ws_o + (row0 + 32 * hb + l32) * kDc;
@@ -608,7 +648,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const f32x4 x = {O[hb][cb][4 * a], O[hb][cb][4 * a + 1], O[hb][cb][4 * a + 2], O[hb][cb][4 * a + 3]};
+          const f32x4 x = f32x4{O[hb][cb][4 * a], O[hb][cb][4 * a + 1], O[hb][cb][4 * a + 2], O[hb][cb][4 * a + 3]} *
+                          e2[cb >> 1];
           f32x4 r;
           if (BITS_C == 4) {  // lower lane: channels 0 2 4 6, upper lane: 1 3 5 7
             const float rx = __shfl_xor(odd ? x[0] : x[2], 32, 64);
@@ -631,18 +672,27 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
 }
 
 template <int BITS_C>
+hipError_t prepare64() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(decode64_kernel<BITS_C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem64<BITS_C>));
+}
+
+template <int BITS_C>
 hipError_t launch64(const DecodeParams& p, hipStream_t stream) {
-  const size_t smem = sizeof(Smem64<BITS_C>);
-  auto kern = decode64_kernel<BITS_C>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
   const int64_t blocks = ((int64_t)p.max_items + 7) / 8 * 8 * p.head_groups;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), smem, stream, p);
-  return hipGetLastError();
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(decode64_kernel<BITS_C>), dim3((unsigned)blocks),
+                         dim3(kThreads), args, sizeof(Smem64<BITS_C>), stream);
 }
 
 }  // namespace
+
+hipError_t prepare_decode64(const DecodeParams&, int bits_c) {
+  if (bits_c == 4) return prepare64<4>();
+  if (bits_c == 2) return prepare64<2>();
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode64(const DecodeParams& p, int bits_c, hipStream_t stream) {
   if (bits_c == 4) return launch64<4>(p, stream);

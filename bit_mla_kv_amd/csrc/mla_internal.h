@@ -25,6 +25,16 @@ __host__ __device__ inline int bf16_token_count(int N, int n_sink, int n_recent)
   return ns + (N - rstart > 0 ? N - rstart : 0);
 }
 
+// Words of the decode workspace header (int32).  plan_kernel writes them at the start of every
+// decode call; the decode kernels add to the counters.
+constexpr int kHdrItems = 0;          // work items of this call
+constexpr int kHdrPagesPerSplit = 1;  // pages per packed chunk
+constexpr int kHdrGiveUps = 4;        // handshake waits between two waves that gave up (bounded wait)
+constexpr int kHdrBadPages = 5;       // page reads whose block-table entry lay outside the table or pool
+constexpr int kHdrBadSeqs = 6;        // sequences with a slot outside the cache or a length outside [0, max_seq_len]
+constexpr int kHdrDropped = 7;        // work items dropped for lack of workspace rows
+constexpr int kDefaultSpin = 1 << 18; // polls of a bounded handshake wait
+
 struct AppendParams {
   uint8_t* pages;
   int64_t num_pages;
@@ -55,6 +65,8 @@ struct DecodeParams {
   const int32_t* seq_slot;
   const int32_t* seq_len;
   int32_t batch, heads;       // heads: rows per sequence = q_len * heads_per_query
+  int32_t max_seq_len;        // the caller's bound on seq_len (sizes the workspace)
+  int32_t spin_limit;         // polls before a handshake wait gives up (counted in the header)
   int32_t q_len;              // query tokens per sequence; row r is query r / heads_per_query
   int32_t heads_per_query;    // a multiple of 16, so a 16-row block belongs to one query
   float scale_log2e;          // softmax_scale * log2(e)
@@ -66,7 +78,7 @@ struct DecodeParams {
   int32_t max_items;          // capacity of items / partial rows
   int32_t* items;             // [max_items] int4 (sequence, first page, pages, kind 0 packed / 1 bf16)
   int32_t* seq_info;          // [batch] int4 (first full item, full items, tail item or -1, bf16 item)
-  int32_t* plan_hdr;          // [0] item count, [1] pages per chunk
+  int32_t* plan_hdr;          // header words kHdr* (item count, pages per chunk, counters)
   float* ws_o;                // [max_items][H][512]: unnormalised partial outputs sum_t 2^(x_t - m) v_t
   float* ws_ml;               // [max_items][H][2]: running max m (log2 domain) and sum l (l = 0: empty)
   float* ws_z;                // [max_items][H][8]: zero-term sums sum_t 2^(x_t - m) z_t,g (has_z)
@@ -75,8 +87,12 @@ struct DecodeParams {
   float* lse;                 // [batch][H] natural log, may be null
 };
 
-// Kernel launchers (each returns the hipError_t of its launch).
+// Kernel launchers (each returns the hipError_t of its launch).  prepare_decode* set the kernel
+// attributes a decode launch needs and check its grid; they enqueue nothing, so the host entry
+// points call them before the first launch of a call.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t prepare_decode(const DecodeParams& p, int bits_c);
+hipError_t prepare_decode64(const DecodeParams& p, int bits_c);
 hipError_t launch_decode(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_decode64(const DecodeParams& p, int bits_c, hipStream_t stream);
 hipError_t launch_decode16(const DecodeParams& p, int bits_c, hipStream_t stream);

@@ -188,13 +188,32 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
     reinterpret_cast<int4*>(p.seq_info)[b] = make_int4(BF + fo[k], nf_cap, ti, bo[k] < p.max_items ? bo[k] : -1);
   }
   if (t == 0) {
-    p.plan_hdr[0] = F + T + BF;  // item count
-    p.plan_hdr[1] = pps;
+    p.plan_hdr[kHdrItems] = F + T + BF;
+    p.plan_hdr[kHdrPagesPerSplit] = pps;
+    p.plan_hdr[kHdrDropped] = max(0, F + T + BF - p.max_items);
+  }
+}
+
+// Sequences whose slot lies outside the cache or whose length lies outside [0, max_seq_len] (they
+// decode as empty, or may not fit the workspace); written to the header with the other counters.
+__device__ void write_counters(const DecodeParams& p, int t) {
+  int bad = 0;
+  for (int b = t; b < p.batch; b += kPlanThreads) {
+    const int N = p.seq_len[b], slot = p.seq_slot[b];
+    bad += (slot < 0 || slot >= p.num_slots || N < 0 || N > p.max_seq_len) ? 1 : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
+  if (t == 0) {
+    p.plan_hdr[kHdrGiveUps] = 0;  // the decode kernels add to these two
+    p.plan_hdr[kHdrBadPages] = 0;
+    p.plan_hdr[kHdrBadSeqs] = bad;
   }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   const int t = threadIdx.x;
+  write_counters(p, t);
   if (p.batch <= kPlanThreads * kPlanRegs) {
     plan_in_registers(p, t);
     return;
@@ -264,8 +283,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     if (BF + fo + nf > p.max_items) p.seq_info[4 * b + 1] = max(0, p.max_items - BF - fo);
   }
   if (t == 0) {
-    p.plan_hdr[0] = F + T + BF;  // item count
-    p.plan_hdr[1] = pps;
+    p.plan_hdr[kHdrItems] = F + T + BF;
+    p.plan_hdr[kHdrPagesPerSplit] = pps;
+    p.plan_hdr[kHdrDropped] = max(0, F + T + BF - p.max_items);
   }
 }
 
@@ -291,7 +311,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
   const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
   const int tl = p.seq_info[4 * b + 2], bi = p.seq_info[4 * b + 3];
   // the sequence's bf16 chunks are consecutive items from bi on (chunks of 64 P tokens)
-  const int nbi = bi < 0 ? 0 : min(bf16_items(seq_bf16_pages(p, b), p.plan_hdr[1]), min(p.plan_hdr[0], p.max_items) - bi);
+  const int nbi = bi < 0 ? 0 : min(bf16_items(seq_bf16_pages(p, b), p.plan_hdr[kHdrPagesPerSplit]),
+                                   min(p.plan_hdr[kHdrItems], p.max_items) - bi);
   const int n_rows = nf + (tl >= 0) + nbi;
   auto item_of = [&](int k) {
     return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi + (k - nf - (tl >= 0)));
@@ -382,15 +403,18 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
 }  // namespace
 
 hipError_t launch_plan(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
-  return hipGetLastError();
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(plan_kernel), dim3(1), dim3(kPlanThreads), args, 0, stream);
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.batch * p.heads;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(64 * kCombineWaves), 0, stream, p);
-  return hipGetLastError();
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(combine_kernel), dim3((unsigned)blocks),
+                         dim3(64 * kCombineWaves), args, 0, stream);
 }
 
 }  // namespace mla

@@ -33,16 +33,52 @@
  *    passed as void*; NULL is the null stream).  An append must be issued
  *    before the decode that reads it, on the same stream (or with a
  *    dependency the caller creates).
- *  - Every entry point returns MLA_LOWBIT_OK or an error status.  Host-side
- *    argument checks run before anything is enqueued; on error nothing is
- *    enqueued and mla_lowbit_last_error() holds a message (thread-local).
- *    Launch failures return MLA_LOWBIT_ERR_DEVICE with the HIP message.
+ *  - Every entry point returns MLA_LOWBIT_OK or an error status, with a
+ *    message in mla_lowbit_last_error() (thread-local).  Argument checks and
+ *    kernel setup run on the host before anything is enqueued; a failure
+ *    there enqueues nothing.  A decode enqueues three kernels (split plan,
+ *    decode, combine); should a later launch fail after an earlier one was
+ *    enqueued, the call returns MLA_LOWBIT_ERR_DEVICE with the HIP message and
+ *    the enqueued kernels write only the workspace, never out or lse.
  *  - Device-resident index data (block_table entries, token positions,
- *    slots, sequence lengths) is the caller's contract: kernels skip writes
- *    and reads whose indices fall outside the buffers described by the
- *    structs, but results for such inputs are unspecified.
- *  - Values are staged through fp16 inside decode: cache rows and queries
- *    must have |x| < 65504 (finite); NaN/Inf inputs are out of contract.
+ *    slots, sequence lengths) is the caller's contract.  The kernels never
+ *    read or write outside the buffers the structs describe: an append skips
+ *    a token whose page entry is out of range, a decode reads page 0 in place
+ *    of an out-of-range page entry and treats a sequence with an out-of-range
+ *    slot as empty; results for such inputs are wrong.  A decode counts these
+ *    events in its workspace (and the bounded waits between the waves of the
+ *    16-head kernel that gave up, which would mean a broken hand-over).
+ *  - Validation mode: with the environment variable MLA_LOWBIT_VALIDATE set
+ *    to a value other than "0" (read at every call), each call first
+ *    synchronises the stream and checks the device-resident index data on
+ *    the host (append: slots in range, 0 <= pos < slot_len_after[slot],
+ *    distinct (slot, pos), written pages inside the table and the pool;
+ *    decode: slots in range, 0 <= seq_len <= max_seq_len, every page read
+ *    from packed copies inside the table and the pool; both: no physical page
+ *    in the tables of two slots), returning MLA_LOWBIT_ERR_INVALID_ARG with
+ *    the offending index before anything is enqueued.  After a decode it
+ *    synchronises again and returns MLA_LOWBIT_ERR_DEVICE when the kernels
+ *    counted any of the events above.  The mode is for debugging: it costs
+ *    host copies of the index data and two stream synchronisations per call.
+ *  - Value range.  Cache rows and queries must be finite with |x| < 65504
+ *    (decode stages codes, bf16 rows, zeros and queries through fp16), and
+ *    |sum over any 64-channel group of q| * softmax_scale < 45000.  Tested
+ *    against the fp64 reference within the bounds below: caches scaled by
+ *    1e-4 .. 300 (group scales from about 2^-15 to 2^13), and magnitudes
+ *    growing by 3e5 along one sequence.  The PV products p * s are formed in
+ *    fp16 with s normalised by a power of two per work item and group, so
+ *    they neither overflow nor fall into subnormals over that range; values
+ *    below 2^-14 in magnitude are carried as fp16 subnormals (absolute
+ *    precision 2^-25).  Probabilities are fp16 (11 significant bits): when
+ *    every score of a long sequence agrees to better than about 2^-11 (in
+ *    log2 units; e.g. queries near zero against small cache values), the
+ *    output is the near-uniform average without the finer weighting, an
+ *    error up to 2^-11 of max |c| that can exceed the bound when max |out|
+ *    is much smaller than max |c|.
+ *  - Accuracy on the workloads' value distributions: max over channels of
+ *    |out - ref| beyond half a bf16 ulp of ref, relative to max |ref| of the
+ *    (sequence, head), <= 2e-3 against an fp64 reference of the same
+ *    selected representations; |lse error| <= 1e-3 + 2^-18 |lse|.
  *
  * Supported layout: d_c = 512, d_r = 64, group = 64, page_tokens = 64,
  * bits_c in {4, 2}, bits_r = 4, 0 <= n_sink <= 64, 1 <= n_recent <= 2^24

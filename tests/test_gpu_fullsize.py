@@ -1,9 +1,7 @@
 """Full-size parity (marked gpu): every workload the benchmark times, at its full size and in the
 launch configuration it times (one quantize-append of a token per sequence, then the decode with the
-default split plan), checked on sampled (sequence, head) outputs that the oracle computes one by one.
-
-Sampled sequences: the first, the last and one drawn from the workload's seed; sampled heads: the
-first, the last and one drawn per sequence.  Each sampled output row is held to the same bound as the
+default split plan), checked on every (sequence, head) output against the oracle, which computes each
+sequence while the cache is being filled.  Every output row is held to the same bound as the
 small-size tests (E <= 2e-3 after the bf16 store, |lse error| <= 1e-3).
 """
 import numpy as np
@@ -12,7 +10,7 @@ import torch
 
 import mla_inputs as mi
 import oracle
-from parity import E_TOL, LSE_TOL, bf16_tensor_to_f64, e_metric
+from parity import E_TOL, bf16_tensor_to_f64, e_metric, lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +24,7 @@ FULL = ["dsv2lite_c4r4_32k", "dsv2lite_c4r4_128k", "dsv3_c4r4_128k", "dsv3_c2r4_
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_every_row(name):
     w = mi.workload(name)
     B, H = w.batch, w.heads
     dev = torch.device("cuda:0")
@@ -36,22 +34,20 @@ def test_full_size_sampled(name):
     perm = mi.page_permutation(w.seed, int(((final + 63) // 64).sum()) + 8)
     cache = cb.allocate_for(layout, start, perm, spare_tokens=1, device=dev)
     outl = mi.outlier_channels(w.seed)
-    pick = np.random.default_rng(1000 + w.seed)
-    seqs = sorted({0, B - 1, int(pick.integers(B))})
     new = np.empty((B, 576), np.uint16)
-    kept = {}
+    q_host = mi.queries(w.seed, B, H)
+    ref_o = np.empty((B, H, 512))
+    ref_l = np.empty((B, H))
     for b in range(B):
         rows = mi.rows(w.seed, b, int(final[b]), outl, threads=16)
         cb.prefill(cache, b, rows[:start[b]])
         new[b] = rows[start[b]]
-        if b in seqs:
-            kept[b] = rows
+        ref_o[b], ref_l[b] = oracle.decode_sequence(rows, q_host[b], w.scale, w.bits_c)
         del rows
     slots = torch.arange(B, dtype=torch.int32, device=dev)
     m.quantize_append(cache, cb.to_device_bf16(new, dev), slots,
                       torch.tensor(start, dtype=torch.int32, device=dev),
                       torch.tensor(final, dtype=torch.int32, device=dev))
-    q_host = mi.queries(w.seed, B, H)
     q = cb.to_device_bf16(q_host.reshape(B * H, -1), dev).view(B, H, 576)
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -62,19 +58,18 @@ def test_full_size_sampled(name):
     o_all = bf16_tensor_to_f64(out)
     l_all = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all)), name
-    for b in seqs:
-        heads = sorted({0, H - 1, int(pick.integers(H))})
-        ro, rl = oracle.decode_sequence(kept[b], q_host[b], w.scale, w.bits_c, heads=heads)
-        E = e_metric(o_all[b, heads], ro)
-        assert E.max() <= E_TOL, f"{name} seq {b} heads {heads}: E {E}"
-        err = np.abs(l_all[b, heads] - rl)
-        assert err.max() <= LSE_TOL, f"{name} seq {b} heads {heads}: lse err {err}"
+    E = e_metric(o_all, ref_o)
+    worst = np.unravel_index(E.argmax(), E.shape)
+    assert E.max() <= E_TOL, f"{name}: E max {E.max():.3e} at (sequence, head) {worst}"
+    err = np.abs(l_all - ref_l)
+    assert np.all(err <= lse_bound(ref_l)), f"{name}: lse err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+    print(f"{name}: {B * H} rows, E max {E.max():.3e}, lse err max {err.max():.3e}", flush=True)
 
 
 def test_full_size_multi_query():
     """Four query tokens per sequence on the 16-head 128K workload (the queries share one read of
-    the cache as one 64-row group): sampled sequences, every query, sampled heads; query i sees the
-    first N - (3 - i) tokens in the representation the cache holds at length N."""
+    the cache as one 64-row group): every sequence, query and head; query i sees the first
+    N - (3 - i) tokens in the representation the cache holds at length N."""
     w = mi.workload("dsv2lite_c4r4_128k")
     B, H, QL = w.batch, w.heads, 4
     dev = torch.device("cuda:0")
@@ -82,15 +77,18 @@ def test_full_size_multi_query():
     layout = m.make_layout(w.bits_c)
     cache = cb.allocate_for(layout, lens, mi.page_permutation(w.seed, int(((lens + 63) // 64).sum()) + 8), device=dev)
     outl = mi.outlier_channels(w.seed)
-    seqs = [0, B - 1]
-    kept = {}
+    q_host = mi.queries(w.seed + 7, B * QL, H).reshape(B, QL, H, 576)
+    ref_o = np.empty((B, QL, H, 512))
+    ref_l = np.empty((B, QL, H))
     for b in range(B):
         rows = mi.rows(w.seed, b, int(lens[b]), outl, threads=16)
         cb.prefill(cache, b, rows)
-        if b in seqs:
-            kept[b] = rows
-        del rows
-    q_host = mi.queries(w.seed + 7, B * QL, H).reshape(B, QL, H, 576)
+        n = rows.shape[0]
+        cc, cr, meta = oracle.quantize(rows, w.bits_c)
+        sel = oracle.select(rows, cc, cr, meta, w.bits_c)
+        for i in range(QL):
+            ref_o[b, i], ref_l[b, i] = oracle.attend(sel[: n - (QL - 1 - i)], q_host[b, i], w.scale)
+        del rows, sel
     q = cb.to_device_bf16(q_host.reshape(B * QL * H, -1), dev).view(B, QL, H, 576)
     out = torch.empty((B, QL, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, QL, H), dtype=torch.float32, device=dev)
@@ -101,25 +99,16 @@ def test_full_size_multi_query():
     o_all = bf16_tensor_to_f64(out)
     l_all = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all))
-    pick = np.random.default_rng(2000 + w.seed)
-    for b in seqs:
-        rows = kept[b]
-        n = rows.shape[0]
-        cc, cr, meta = oracle.quantize(rows, w.bits_c)
-        sel = oracle.select(rows, cc, cr, meta, w.bits_c)
-        heads = sorted({0, H - 1, int(pick.integers(H))})
-        for i in range(QL):
-            ro, rl = oracle.attend(sel[: n - (QL - 1 - i)], q_host[b, i], w.scale, heads=heads)
-            E = e_metric(o_all[b, i, heads], ro)
-            assert E.max() <= E_TOL, f"seq {b} query {i} heads {heads}: E {E}"
-            assert np.abs(l_all[b, i, heads] - rl).max() <= LSE_TOL, f"seq {b} query {i}"
+    E = e_metric(o_all, ref_o)
+    assert E.max() <= E_TOL, f"E max {E.max():.3e} at (sequence, query, head) {np.unravel_index(E.argmax(), E.shape)}"
+    assert np.all(np.abs(l_all - ref_l) <= lse_bound(ref_l))
 
 
 @pytest.mark.parametrize("heads,bits_c", [(128, 4), (16, 2)])
 def test_million_token_context(heads, bits_c):
     """The longest context of the pages' latency sweep (1M tokens), beside a short sequence in the
     same batch: one 1,048,576-token sequence and one of 777 tokens, decoded with the default split
-    plan (the long one split over every CU, the short one in one or two items).  Sampled heads of
+    plan (the long one split over every CU, the short one in one or two items).  Every head of
     both sequences against the oracle, same bounds as above."""
     seed = 11 + bits_c
     lens = np.array([1 << 20, 777], np.int64)
@@ -146,11 +135,10 @@ def test_million_token_context(heads, bits_c):
     o_all = bf16_tensor_to_f64(out)
     l_all = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all))
-    pick = np.random.default_rng(2000 + seed)
     for b in range(B):
-        hs = sorted({0, heads - 1, int(pick.integers(heads))})
+        hs = list(range(heads))
         ro, rl = oracle.decode_sequence(kept[b], q_host[b], scale, bits_c, heads=hs)
         E = e_metric(o_all[b, hs], ro)
         assert E.max() <= E_TOL, f"H{heads} C{bits_c} seq {b} heads {hs}: E {E}"
         err = np.abs(l_all[b, hs] - rl)
-        assert err.max() <= LSE_TOL, f"H{heads} C{bits_c} seq {b} heads {hs}: lse err {err}"
+        assert np.all(err <= lse_bound(rl)), f"H{heads} C{bits_c} seq {b}: lse err {err.max():.3e}"
