@@ -56,6 +56,8 @@ def _load():
     L.mla_lowbit_decode_multi.argtypes = [ctypes.POINTER(CacheDesc), P, P, P, I32, I32, I32, I32, ctypes.c_float,
                                           P, P, P, SZ, P]
     L.mla_lowbit_decode_multi.restype = ctypes.c_int
+    L.mla_lowbit_decode_noalloc.argtypes = [ctypes.POINTER(CacheDesc), P, P, P, I32, I32, I32, ctypes.c_float, P, P, P]
+    L.mla_lowbit_decode_noalloc.restype = ctypes.c_int
     L.mla_lowbit_status_string.argtypes = [ctypes.c_int]
     L.mla_lowbit_status_string.restype = ctypes.c_char_p
     L.mla_lowbit_profile_decode_events.argtypes = [P, P]
@@ -67,8 +69,9 @@ def _load():
 
 lib = _load()
 EXPORTS = ("mla_lowbit_page_bytes", "mla_lowbit_quantize_append", "mla_lowbit_decode_workspace_bytes",
-           "mla_lowbit_decode", "mla_lowbit_decode_multi", "mla_lowbit_profile_decode_events", "mla_lowbit_status_string",
-           "mla_lowbit_last_error")
+           "mla_lowbit_decode", "mla_lowbit_decode_multi", "mla_lowbit_decode_noalloc", "mla_lowbit_profile_decode_events",
+           "mla_lowbit_status_string", "mla_lowbit_last_error")
+SCRATCH_BYTES = 80 << 20  # MLA_LOWBIT_SCRATCH_BYTES
 
 
 def _check(status: int) -> None:
@@ -163,6 +166,16 @@ def decode_multi(cache: PagedCache, q: torch.Tensor, seq_slot: torch.Tensor, seq
     _check(lib.mla_lowbit_decode_multi(ctypes.byref(d), _ptr(q), _ptr(seq_slot), _ptr(seq_len), batch, q_len, heads,
                                        max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_noalloc(cache: PagedCache, q: torch.Tensor, seq_slot: torch.Tensor, seq_len: torch.Tensor,
+                   max_seq_len: int, softmax_scale: float, out: torch.Tensor, lse: torch.Tensor | None,
+                   stream=None) -> None:
+    """mla_lowbit_decode_noalloc: mla_lowbit_decode on the library's built-in device scratch."""
+    batch, heads = q.shape[0], q.shape[1]
+    d = cache.desc
+    _check(lib.mla_lowbit_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(seq_slot), _ptr(seq_len), batch, heads,
+                                         max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def alloc_workspace(layout: Layout, batch: int, heads: int, max_seq_len: int, device="cuda") -> torch.Tensor:

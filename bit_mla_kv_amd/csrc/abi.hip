@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -206,6 +207,39 @@ WsLayout ws_layout(int batch, int heads, int max_items) {
 
 }  // namespace
 
+// Built-in decode workspace of mla_lowbit_decode_noalloc: one copy on every GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is taken with hipGetSymbolAddress (per device, below) and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_LOWBIT_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each device, once resolved
+
+// The scratch address on the current device, resolved on the first call made with that device
+// current.
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  int st = device_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != MLA_LOWBIT_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_LOWBIT_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    st = device_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != MLA_LOWBIT_OK) return st;
+    if (!ptr) return fail(MLA_LOWBIT_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_LOWBIT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t mla_lowbit_page_bytes(const mla_lowbit_layout* layout) {
@@ -264,7 +298,7 @@ int mla_lowbit_profile_decode_events(void* start, void* stop) {
 static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
                        int32_t batch, int32_t q_len, int32_t heads_per_query, int32_t max_seq_len,
                        float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                       void* stream, hipEvent_t ev0, hipEvent_t ev1) {
+                       void* stream, hipEvent_t ev0, hipEvent_t ev1, bool allow_validate = true) {
   int st = check_cache(cache);
   if (st != MLA_LOWBIT_OK) return st;
   if (batch < 0 || max_seq_len < 0)
@@ -330,7 +364,7 @@ static int decode_impl(const mla_lowbit_cache* cache, const void* q, const int32
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool validate = validate_mode();
+  const bool validate = allow_validate && validate_mode();
   if (validate && (st = validate_decode_inputs(cache, seq_slot, seq_len, batch, max_seq_len, s)) != MLA_LOWBIT_OK)
     return st;
   // everything a launch of this call can be refused for is checked before the first one
@@ -364,6 +398,23 @@ int mla_lowbit_decode_multi(const mla_lowbit_cache* cache, const void* q, const 
   g_prof_start = g_prof_stop = nullptr;
   return decode_impl(cache, q, seq_slot, seq_len, batch, q_len, num_heads, max_seq_len, softmax_scale, out, lse,
                      workspace, workspace_bytes, stream, ev0, ev1);
+}
+
+int mla_lowbit_decode_noalloc(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot,
+                              const int32_t* seq_len, int32_t batch, int32_t num_heads, int32_t max_seq_len,
+                              float softmax_scale, void* out, float* lse, void* stream) {
+  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  int st = check_cache(cache);
+  if (st != MLA_LOWBIT_OK) return st;
+  const size_t need = mla_lowbit_decode_workspace_bytes(&cache->layout, batch, num_heads, max_seq_len);
+  if (need > MLA_LOWBIT_SCRATCH_BYTES)
+    return fail(MLA_LOWBIT_ERR_WORKSPACE, "this shape needs %zu workspace bytes; the built-in scratch holds %zu",
+                need, (size_t)MLA_LOWBIT_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != MLA_LOWBIT_OK) return st;
+  return decode_impl(cache, q, seq_slot, seq_len, batch, 1, num_heads, max_seq_len, softmax_scale, out, lse, ws,
+                     MLA_LOWBIT_SCRATCH_BYTES, stream, ev0, ev1, /*allow_validate=*/false);
 }
 
 }  // extern "C"

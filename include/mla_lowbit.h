@@ -230,6 +230,30 @@ int mla_lowbit_decode_multi(const mla_lowbit_cache* cache, const void* q, const 
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments and results as mla_lowbit_decode, without
+ * workspace / workspace_bytes: the library uses its built-in scratch, a
+ * file-scope device array of MLA_LOWBIT_SCRATCH_BYTES (80 MiB) that every GPU
+ * the library runs on holds until the process ends (its address is resolved
+ * on the first call made with that device current).
+ *  - Returns MLA_LOWBIT_ERR_WORKSPACE when mla_lowbit_decode_workspace_bytes()
+ *    for this shape exceeds MLA_LOWBIT_SCRATCH_BYTES (e.g. 128 heads: up to
+ *    64 sequences of any length; 16 heads: several hundred).
+ *  - Allocates nothing and calls no allocating routine; the validation mode
+ *    does not apply to it (the counters are still written to the scratch).
+ *  - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *    call's contents and needs no clearing (each call writes what it reads).
+ *    Calls ordered on one stream are safe; calls that overlap on one GPU (on
+ *    different streams, or from threads without ordering between them) race
+ *    and give wrong results.
+ */
+#define MLA_LOWBIT_SCRATCH_BYTES ((size_t)80 << 20)
+int mla_lowbit_decode_noalloc(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot,
+                              const int32_t* seq_len, int32_t batch, int32_t num_heads, int32_t max_seq_len,
+                              float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * Measurement aid (not needed for decoding).  Arms two caller-created HIP
  * events (hipEvent_t passed as void*) for the NEXT mla_lowbit_decode or
  * mla_lowbit_decode_multi call on this thread: that call records `start` on
