@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
     auto block_qk = [&](auto&& kw, auto&& kf16, const uint32_t* mw, bool valid, bool codes, int so) -> f32x4 {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
+      for (int i = 0; i < kGroups; ++i) {  // groups 8 (RoPE key), 0, 1, .., 7: the RoPE-key product first
+        const int g = i == 0 ? kGroups - 1 : i - 1;
         f16x8 k0, k1;
         if (codes) {
           const u32x2 v = kw(g);

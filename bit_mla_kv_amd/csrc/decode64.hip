@@ -378,18 +378,22 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         constexpr int kAhead = 3;
         f16x8 kf[kAhead][4];
         f32x2 scf[kAhead];
-        auto request = [&](int g) {
-          kf[g % kAhead][0] = lds_load<f16x8>(k0 + 64 * g);
-          kf[g % kAhead][1] = lds_load<f16x8>(k1 + 64 * g);
-          kf[g % kAhead][2] = lds_load<f16x8>(k0 + 64 * g + 32);
-          kf[g % kAhead][3] = lds_load<f16x8>(k1 + 64 * g + 32);
-          scf[g % kAhead] = lds_load<f32x2>(sqp + g * kT);
+        // groups in the order 8 (RoPE key), 0, 1, .., 7: the RoPE-key product is requested and
+        // issued first
+        auto grp = [](int i) { return i == 0 ? kGroups - 1 : i - 1; };
+        auto request = [&](int i) {
+          const int g = grp(i);
+          kf[i % kAhead][0] = lds_load<f16x8>(k0 + 64 * g);
+          kf[i % kAhead][1] = lds_load<f16x8>(k1 + 64 * g);
+          kf[i % kAhead][2] = lds_load<f16x8>(k0 + 64 * g + 32);
+          kf[i % kAhead][3] = lds_load<f16x8>(k1 + 64 * g + 32);
+          scf[i % kAhead] = lds_load<f32x2>(sqp + g * kT);
         };
 #pragma unroll
-        for (int g = 0; g < kAhead; ++g) request(g);
+        for (int i = 0; i < kAhead; ++i) request(i);
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          const int r = g % kAhead;
+        for (int i = 0; i < kGroups; ++i) {
+          const int g = grp(i), r = i % kAhead;
           const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
           f32x4 c0 = mfma16(qreg[2 * g], kf[r][0], z4);
           f32x4 c1 = mfma16(qreg[2 * g], kf[r][1], z4);
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           c1 = mfma16(qreg[2 * g + 1], kf[r][3], c1);
           const f32x2 sc = scf[r];
           __builtin_amdgcn_sched_barrier(0);
-          if (g + kAhead < kGroups) request(g + kAhead);
+          if (i + kAhead < kGroups) request(i + kAhead);
           __builtin_amdgcn_sched_barrier(0);
           s[0] += sc[0] * c0;
           s[1] += sc[1] * c1;
