@@ -99,6 +99,10 @@ __device__ __forceinline__ f16x4 lds_tr4(lds_ptr<f16> p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+__device__ __forceinline__ f16x8 cat8(f16x4 lo, f16x4 hi) {
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
