@@ -17,7 +17,8 @@
 //  - the PV wave loads a block's content words one block ahead with
 //    contiguous 16-byte loads, writes the codes to the pair's tile as one byte
 //    per code, and for every block the QK wave has scored accumulates MFMA
-//    16x16x32 f16 of the codes (8-bit transposed LDS reads, converted exactly)
+//    16x16x32 f16 of the codes (8-bit transposed LDS reads, widened exactly to
+//    fp16 subnormals)
 //    against p * s_g, plus the zero terms sum_t p_t z_g,t;
 //  - the QK wave multiplies the tile's code bytes by the query with MFMA
 //    16x16x64 i8: the query in fixed point, three int8 digits per component,
@@ -75,8 +76,8 @@ struct MergeArea {          // merge of the pairs' partials at the end (two pair
 };
 
 // Packed items run in 32-token blocks (half a page) whose codes sit in LDS one byte each: code c
-// (0..15) is the byte c (the int8 c to the QK MFMA, the e4m3 value c * 2^-9 to the PV
-// conversion).  A token row holds 32 units of 16 code bytes; unit u covers the 16 channels from pk_unit_base(u) on, byte b of it channel
+// (0..15) is the byte c (the int8 c to the QK MFMA; zero-extended to 16 bits, the fp16 c * 2^-24
+// to the PV MFMA, whose sums are scaled back by 2^24 at the end).  A token row holds 32 units of 16 code bytes; unit u covers the 16 channels from pk_unit_base(u) on, byte b of it channel
 // pk_unit_base(u) + pk_unit_off(b), an order that lets the unpacking write whole units and lets
 // both multiplications read them directly.
 constexpr int kPB = 32;    // tokens per packed block
@@ -151,9 +152,9 @@ __device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
 
 // ---- merge of the four pairs' partials, shared by both item kinds.  The QK wave of pair pr gives
 // its running maxima and sums; the PV wave brings its accumulators to the merged maximum (and
-// multiplies them by 2^cur_e, undoing the PV scale normaliser), the pairs' outputs are summed
-// through LDS into pair 0, which passes them to write() and stores the running max, sum and the
-// zero-term sums of the split's row.  Both roles pass five workgroup barriers.
+// multiplies them by 2^cur_e, undoing the PV scale normaliser and the codes' operand scale), the
+// pairs' outputs are summed through LDS into pair 0, which passes them to write() and stores the
+// running max, sum and the zero-term sums of the split's row.  Both roles pass five workgroup barriers.
 __device__ __forceinline__ void merge_qk(MergeArea& mg, const float (&m_run)[4], const float (&l_part)[4], int pr,
                                          int G, int L16) {
   __syncthreads();  // every wave is done with its tiles; the merge area overlays them
@@ -182,7 +183,7 @@ __device__ __forceinline__ void merge_pv(const DecodeParams& p, MergeArea& mg, f
   {
     const float mw = mg.m[pr][L16];
     const float f = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    const float fe = f * __builtin_ldexpf(1.f, cur_e);  // undo the PV scale normaliser
+    const float fe = __builtin_ldexpf(f, cur_e);  // undo the PV scale normaliser (f <= 1)
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) O[cb] *= fe;
     oz *= f;
@@ -277,14 +278,14 @@ __device__ __forceinline__ f32x4 mfma32k_acc(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 code bytes (a tr_b8 column: 8 tokens of one channel) -> 8 fp16 codes: read as e4m3, byte c
-// (c <= 15) is the value c * 2^-9 exactly, and the conversion's scale 2^9 gives back c
-__device__ __forceinline__ f16x8 fp8x8_to_f16(u32x2 v) {
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 512.0f, false);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 512.0f, true);
-  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 512.0f, false);
-  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 512.0f, true);
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+// 8 code bytes (a tr_b8 column: 8 tokens of one channel) -> 8 fp16 operands: each byte c (c <= 15)
+// zero-extended to 16 bits, the fp16 subnormal c * 2^-24 exactly (one byte permute per two codes).
+// The MFMA keeps fewer bits of products with subnormal operands (relative error about 2^-18 of the
+// summed magnitudes instead of 2^-24), ample for the PV sums but not for the scores.
+__device__ __forceinline__ f16x8 codes_to_f16(u32x2 v) {
+  const uint32_t a = __builtin_amdgcn_perm(0u, v.x, 0x0c010c00u), b = __builtin_amdgcn_perm(0u, v.x, 0x0c030c02u);
+  const uint32_t c = __builtin_amdgcn_perm(0u, v.y, 0x0c010c00u), d = __builtin_amdgcn_perm(0u, v.y, 0x0c030c02u);
+  return __builtin_bit_cast(f16x8, u32x4{a, b, c, d});
 }
 
 struct ItemCtx {
@@ -296,7 +297,7 @@ struct ItemCtx {
 //  - the PV wave (pr + 4) loads a block's content codes with contiguous 16-byte loads one block
 //    ahead, turns them into code bytes and writes them to the pair's code tile; for every block
 //    the QK wave has scored it accumulates MFMA 16x16x32 f16 of the codes (8-bit transposed LDS
-//    reads, converted with a 2^9 scale) against p * s_g * 2^-E, and the zero-term sums;
+//    reads, widened to fp16 subnormals c * 2^-24) against p * s_g * 2^-E, and the zero-term sums;
 //  - the QK wave (pr) multiplies the tile's code bytes by the queries with MFMA 16x16x64 i8: each
 //    head's query, times a power of two that puts its largest component in [2^19, 2^20), is rounded
 //    to an integer (exact for every component above 2^-12 of the largest, which bf16 holds with 8
@@ -692,7 +693,7 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int u = qk_unit<BITS_C>(g, q);
-          O[u] = mfma32k_acc(fp8x8_to_f16(raw[g & 1][q]), bop, O[u]);
+          O[u] = mfma32k_acc(codes_to_f16(raw[g & 1][q]), bop, O[u]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -720,7 +721,7 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
     }
     if (lane == 0 && give_ups) atomicAdd(p.plan_hdr + kHdrGiveUps, give_ups);
     const int64_t orow = (int64_t)it.item * p.heads + it.head0 + L16;
-    merge_pv(p, s_tiles.mg, O, oz, cur_e, pr, lane, G, L16, orow, [&](f32x4(&Of)[32]) {
+    merge_pv(p, s_tiles.mg, O, oz, cur_e + 24, pr, lane, G, L16, orow, [&](f32x4(&Of)[32]) {
       float* dst = p.ws_o + orow * kDc;
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
