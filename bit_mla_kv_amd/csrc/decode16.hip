@@ -127,28 +127,6 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + __shfl_xor(v, 8, 64);
 }
 
-// Handshake flags live in an LDS object of their own, read and written as volatile words.
-typedef __attribute__((address_space(3))) volatile int lds_vint;
-// Returns 1 when the wait gave up after `spin` polls (counted into the workspace header).
-// The empty asm with a memory clobber keeps the compiler from moving the LDS reads of the data the
-// flag guards above the wait.
-__device__ __forceinline__ int wait_at_least(lds_vint* flag, int target, int spin) {
-  int gave_up = 1;
-  for (int i = 0; i < spin; ++i) {
-    if (__builtin_amdgcn_readfirstlane(*flag) >= target) {
-      gave_up = 0;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("" ::: "memory");
-  return gave_up;
-}
-// publish a flag value once this wave's earlier LDS writes have completed
-__device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane == 0) *flag = value;
-}
 
 // ---- merge of the four pairs' partials, shared by both item kinds.  The QK wave of pair pr gives
 // its running maxima and sums; the PV wave brings its accumulators to the merged maximum (and

@@ -109,5 +109,29 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float fmax4(f32x4 v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
 
+
+// Handshake flags between the waves of a workgroup live in LDS, read and written as volatile words.
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+// Returns 1 when the wait gave up after `spin` polls (counted into the workspace header).
+// The empty asm with a memory clobber keeps the compiler from moving the LDS reads of the data the
+// flag guards above the wait.
+__device__ __forceinline__ int wait_at_least(lds_vint* flag, int target, int spin) {
+  int gave_up = 1;
+  for (int i = 0; i < spin; ++i) {
+    if (__builtin_amdgcn_readfirstlane(*flag) >= target) {
+      gave_up = 0;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  return gave_up;
+}
+// publish a flag value once this wave's earlier LDS writes have completed
+__device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) *flag = value;
+}
+
 }  // namespace dev
 }  // namespace mla

@@ -299,36 +299,44 @@ __device__ __forceinline__ uint16_t f2bf_rne(float f) {
 // w, w + 4, ... over all 512 channels (8 per lane), eight rows at a time with every load
 // requested before use, as a running max-shifted sum; the four waves' sums are then joined
 // through LDS.
-constexpr int kCombineWaves = 4;
-__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParams p) {
+constexpr int kCombineWaves = 4;  // waves per workgroup
+// rw waves per output row (sequence b, head h), 4 / rw rows per workgroup: wave w takes row
+// blockIdx.x * (4 / rw) + w / rw and, of that row's partials (one per work item of the sequence),
+// those with index = w % rw modulo rw, eight at a time, merged with a running max; the waves of a
+// row are joined through LDS.  Lane l holds channels 4 l .. 4 l + 3 (group l / 16) and
+// 256 + 4 l .. (group 4 + l / 16).  rw (1, 2 or 4) is chosen on the host so that a launch has a
+// few thousand waves in flight: one per row when the rows are many, four when they are few (and
+// their partials many).
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParams p, int rw) {
   constexpr int kBatch = 8;
   __shared__ float sh_m[kCombineWaves], sh_d[kCombineWaves];
-  __shared__ f32x4 sh_acc[kCombineWaves - 1][2][64];
-  const int b = blockIdx.x / p.heads;
-  const int h = blockIdx.x % p.heads;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  __shared__ f32x4 sh_acc[kCombineWaves][2][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = w % rw, w0 = w - sub;  // w0: the row's first wave
+  const int64_t rid = (int64_t)blockIdx.x * (kCombineWaves / rw) + w / rw;
+  const bool live = rid < (int64_t)p.batch * p.heads;
+  const int b = live ? (int)(rid / p.heads) : 0;
+  const int h = live ? (int)(rid % p.heads) : 0;
   const int fo = p.seq_info[4 * b + 0], nf = p.seq_info[4 * b + 1];
   const int tl = p.seq_info[4 * b + 2], bi = p.seq_info[4 * b + 3];
   // the sequence's bf16 chunks are consecutive items from bi on (chunks of 64 P tokens)
   const int nbi = bi < 0 ? 0 : min(bf16_items(seq_bf16_pages(p, b), p.plan_hdr[kHdrPagesPerSplit]),
                                    min(p.plan_hdr[kHdrItems], p.max_items) - bi);
-  const int n_rows = nf + (tl >= 0) + nbi;
+  const int n_rows = live ? nf + (tl >= 0) + nbi : 0;
   auto item_of = [&](int k) {
     return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi + (k - nf - (tl >= 0)));
   };
-  // lane's channels: 4 lane .. 4 lane + 3 (group lane / 16) and 256 + 4 lane .. (group 4 + lane / 16)
   const int g0 = lane / 16, g1 = 4 + lane / 16;
 
   float M = -__builtin_inff(), den = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int my_rows = n_rows > w ? (n_rows - w + kCombineWaves - 1) / kCombineWaves : 0;
+  const int my_rows = n_rows > sub ? (n_rows - sub + rw - 1) / rw : 0;
   for (int j0 = 0; j0 < my_rows; j0 += kBatch) {
     float mv[kBatch], lv[kBatch];
     f32x4 ov0[kBatch], ov1[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int k = w + kCombineWaves * min(j0 + j, my_rows - 1);  // past the end: last row, weight 0
+      const int k = sub + rw * min(j0 + j, my_rows - 1);  // past the end: the last row again, weight 0
       const int64_t row = (int64_t)item_of(k) * p.heads + h;
       mv[j] = p.ws_ml[2 * row];
       lv[j] = j0 + j < my_rows ? p.ws_ml[2 * row + 1] : 0.f;
@@ -358,46 +366,51 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
       acc1 += wgt * ov1[j];
     }
   }
-  // join the four waves' sums in wave 0
-  if (lane == 0) {
-    sh_m[w] = M;
-    sh_d[w] = den;
-  }
-  if (w > 0) {
-    sh_acc[w - 1][0][lane] = acc0;
-    sh_acc[w - 1][1][lane] = acc1;
-  }
-  __syncthreads();
-  if (w != 0) return;
-  float Mt = M;
-#pragma unroll
-  for (int v = 1; v < kCombineWaves; ++v) Mt = fmaxf(Mt, sh_m[v]);
-  float L = -__builtin_inff();
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-  if (Mt != -__builtin_inff()) {
-    float dt = 0.f;
-#pragma unroll
-    for (int v = 0; v < kCombineWaves; ++v) {
-      const float mv = v == 0 ? M : sh_m[v];
-      if (mv == -__builtin_inff()) continue;
-      const float f = __builtin_amdgcn_exp2f(mv - Mt);
-      dt += f * (v == 0 ? den : sh_d[v]);
-      o0 += f * (v == 0 ? acc0 : sh_acc[v - 1][0][lane]);
-      o1 += f * (v == 0 ? acc1 : sh_acc[v - 1][1][lane]);
+  if (rw > 1) {  // join the row's waves in its first wave
+    if (lane == 0) {
+      sh_m[w] = M;
+      sh_d[w] = den;
     }
-    o0 *= 1.f / dt;
-    o1 *= 1.f / dt;
-    L = Mt + __log2f(dt);
+    sh_acc[w][0][lane] = acc0;
+    sh_acc[w][1][lane] = acc1;
+    __syncthreads();
+    if (sub != 0) return;
+    float Mt = M;
+    for (int v = 1; v < rw; ++v) Mt = fmaxf(Mt, sh_m[w0 + v]);
+    if (Mt != -__builtin_inff()) {
+      float dt = 0.f;
+      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < rw; ++v) {
+        const float mv = sh_m[w0 + v];
+        if (mv == -__builtin_inff()) continue;
+        const float f = __builtin_amdgcn_exp2f(mv - Mt);
+        dt += f * sh_d[w0 + v];
+        o0 += f * sh_acc[w0 + v][0][lane];
+        o1 += f * sh_acc[w0 + v][1][lane];
+      }
+      M = Mt;
+      den = dt;
+      acc0 = o0;
+      acc1 = o1;
+    }
   }
-  uint16_t* o = p.out + ((int64_t)b * p.heads + h) * kDc;
+  if (!live) return;
+  float L = -__builtin_inff();
+  if (M != -__builtin_inff()) {
+    const float inv = 1.f / den;
+    acc0 *= inv;
+    acc1 *= inv;
+    L = M + __log2f(den);
+  }
+  uint16_t* o = p.out + rid * kDc;
   uint2 q0, q1;
-  q0.x = (uint32_t)f2bf_rne(o0[0]) | ((uint32_t)f2bf_rne(o0[1]) << 16);
-  q0.y = (uint32_t)f2bf_rne(o0[2]) | ((uint32_t)f2bf_rne(o0[3]) << 16);
-  q1.x = (uint32_t)f2bf_rne(o1[0]) | ((uint32_t)f2bf_rne(o1[1]) << 16);
-  q1.y = (uint32_t)f2bf_rne(o1[2]) | ((uint32_t)f2bf_rne(o1[3]) << 16);
+  q0.x = (uint32_t)f2bf_rne(acc0[0]) | ((uint32_t)f2bf_rne(acc0[1]) << 16);
+  q0.y = (uint32_t)f2bf_rne(acc0[2]) | ((uint32_t)f2bf_rne(acc0[3]) << 16);
+  q1.x = (uint32_t)f2bf_rne(acc1[0]) | ((uint32_t)f2bf_rne(acc1[1]) << 16);
+  q1.y = (uint32_t)f2bf_rne(acc1[2]) | ((uint32_t)f2bf_rne(acc1[3]) << 16);
   *reinterpret_cast<uint2*>(o + 4 * lane) = q0;
   *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = q1;
-  if (p.lse && lane == 0) p.lse[(int64_t)b * p.heads + h] = L * 0.69314718055994531f;
+  if (p.lse && lane == 0) p.lse[rid] = L * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -409,10 +422,13 @@ hipError_t launch_plan(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.batch * p.heads;
-  if (blocks == 0) return hipSuccess;
+  const int64_t rows = (int64_t)p.batch * p.heads;
+  if (rows == 0) return hipSuccess;
+  const int rw = rows >= 4096 ? 1 : rows >= 2048 ? 2 : 4;  // waves per row
+  const int64_t blocks = (rows * rw + kCombineWaves - 1) / kCombineWaves;
   DecodeParams arg = p;
-  void* args[] = {&arg};
+  int rw_arg = rw;
+  void* args[] = {&arg, &rw_arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(combine_kernel), dim3((unsigned)blocks),
                          dim3(64 * kCombineWaves), args, 0, stream);
 }
