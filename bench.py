@@ -133,8 +133,22 @@ def cpu_baseline(w, budget_s):
         if t_used >= budget_s:
             break
     return {"value": tokens / t_used, "unit": "KV tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{seqs} sequence(s) x {heads_done} heads, {tokens} context tokens, quantize+select+"
                       f"fp64 attention, {t_used:.1f} s wall"}
+
+
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def source_digest():
