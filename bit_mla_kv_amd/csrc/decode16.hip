@@ -132,7 +132,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 // its running maxima and sums; the PV wave brings its accumulators to the merged maximum (and
 // multiplies them by 2^cur_e, undoing the PV scale normaliser and the codes' operand scale), the
 // pairs' outputs are summed through LDS into pair 0, which passes them to write() and stores the
-// running max, sum and the zero-term sums of the split's row.  Both roles pass five workgroup barriers.
+// running max, sum and the zero-term sums of the split's row.  When the item is its sequence's only
+// one (direct), pair 0 instead has write() store the final bf16 outputs (sum plus the group's zero
+// term, over the sum of probabilities) and stores the lse, as the combine would.  Both roles pass
+// five workgroup barriers.
 __device__ __forceinline__ void merge_qk(MergeArea& mg, const float (&m_run)[4], const float (&l_part)[4], int pr,
                                          int G, int L16) {
   __syncthreads();  // every wave is done with its tiles; the merge area overlays them
@@ -152,7 +155,8 @@ __device__ __forceinline__ void merge_qk(MergeArea& mg, const float (&m_run)[4],
 
 template <typename Write>
 __device__ __forceinline__ void merge_pv(const DecodeParams& p, MergeArea& mg, f32x4 (&O)[32], f32x4 oz, int cur_e,
-                                         int pr, int lane, int G, int L16, int64_t orow, Write write) {
+                                         int pr, int lane, int G, int L16, int64_t orow, bool direct,
+                                         int64_t out_row, Write write) {
   __syncthreads();  // every wave is done with its tiles; the merge area overlays them
   __syncthreads();  // the QK waves' running maxima and sums are in place
   float M = -__builtin_inff();  // merged max of head L16 (the PV column)
@@ -191,20 +195,26 @@ __device__ __forceinline__ void merge_pv(const DecodeParams& p, MergeArea& mg, f
   __syncthreads();
   if (pr == 0) {
     add(0);
-    write(O);
-    if (G == 0) {
-      float L = 0.f, zs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f, zs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // of head L16
 #pragma unroll
-      for (int v = 0; v < kPairs; ++v) {
-        const float mv = mg.m[v][L16];
-        L += (mv == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv - M)) * mg.l[v][L16];
+    for (int v = 0; v < kPairs; ++v) {
+      const float mv = mg.m[v][L16];
+      L += (mv == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv - M)) * mg.l[v][L16];
 #pragma unroll
-        for (int g = 0; g < 8; ++g) zs[g] += mg.z[v][L16][g];
+      for (int g = 0; g < 8; ++g) zs[g] += mg.z[v][L16][g];
+    }
+    if (direct) {
+      write(O, zs, M == -__builtin_inff() ? 0.f : 1.f / L);
+      if (G == 0 && p.lse)
+        p.lse[out_row] = M == -__builtin_inff() ? -__builtin_inff() : (M + __log2f(L)) * 0.69314718055994531f;
+    } else {
+      write(O, zs, 0.f);
+      if (G == 0) {
+        p.ws_ml[2 * orow] = M;
+        p.ws_ml[2 * orow + 1] = L;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) p.ws_z[orow * 8 + g] = zs[g];
       }
-      p.ws_ml[2 * orow] = M;
-      p.ws_ml[2 * orow + 1] = L;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) p.ws_z[orow * 8 + g] = zs[g];
     }
   }
 }
@@ -699,7 +709,8 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
     }
     if (lane == 0 && give_ups) atomicAdd(p.plan_hdr + kHdrGiveUps, give_ups);
     const int64_t orow = (int64_t)it.item * p.heads + it.head0 + L16;
-    merge_pv(p, s_tiles.mg, O, oz, cur_e + 24, pr, lane, G, L16, orow, [&](f32x4(&Of)[32]) {
+    merge_pv(p, s_tiles.mg, O, oz, cur_e + 24, pr, lane, G, L16, orow, false, 0,
+             [&](f32x4(&Of)[32], const float(&)[8], float) {
       float* dst = p.ws_o + orow * kDc;
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
@@ -994,8 +1005,14 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
     }
     if (lane == 0 && give_ups) atomicAdd(p.plan_hdr + kHdrGiveUps, give_ups);
     const int64_t orow = (int64_t)item * p.heads + head0 + L16;
-    merge_pv(p, mg, O, oz, 0, pr, lane, G, L16, orow, [&](f32x4(&Of)[32]) {
+    // a sequence decoded by this item alone gets its final outputs here (workgroup-uniform)
+    const bool direct = decoded_in_one_item(p, b);
+    if (direct && pr == 0 && lane == 0) atomicAdd(p.plan_hdr + kHdrDirect, 1);  // (PV waves run this)
+    const int64_t out_row = (int64_t)b * p.heads + head0 + L16;
+    merge_pv(p, mg, O, oz, 0, pr, lane, G, L16, orow, direct, out_row,
+             [&](f32x4(&Of)[32], const float(&zs)[8], float inv) {
       float* dst = p.ws_o + orow * kDc;
+      uint16_t* od = p.out + out_row * kDc;
       // Lanes G and G ^ 1 (lane ^ 16) hold the 8 channels 16 cb + 8 (G >> 1) + 0..7 between them,
       // in the unpacking order; each takes two values from the other so that lane G even holds
       // channels 0..3 and lane G odd channels 4..7, written as one 16-byte store.
@@ -1013,7 +1030,9 @@ __global__ __launch_bounds__(kThreads) void decode16_kernel(DecodeParams p) {
           const float ry = __shfl_xor(odd ? v[2] : v[3], 16, 64);
           r = odd ? f32x4{rx, ry, v[1], v[3]} : f32x4{v[0], v[2], rx, ry};
         }
-        *reinterpret_cast<f32x4*>(dst + 16 * cb + 8 * (G >> 1) + 4 * (G & 1)) = r;
+        const int c0 = 16 * cb + 8 * (G >> 1) + 4 * (G & 1);  // channels c0 .. c0 + 3, group cb / 4
+        if (direct) store_bf16x4(od + c0, (r + zs[cb >> 2]) * inv);
+        else *reinterpret_cast<f32x4*>(dst + c0) = r;
       }
     });
   }

@@ -202,6 +202,14 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   const int head0 = hg * kHW;
   const float c_log2 = p.scale_log2e;
   const int64_t row0 = (int64_t)item * p.heads + head0;  // first workspace row of this workgroup
+  // A sequence decoded by this item alone (a bf16 item, no packed chunk) gets its final outputs
+  // and lse here, as the combine would compute them from this one partial: the QK waves hand each
+  // head's running max and sum, the PV waves the zero-term sums, through the then unused tile
+  // slot 0 (one more workgroup barrier, taken by every wave).
+  const bool direct = !packed && decoded_in_one_item(p, b);
+  const int64_t orow0 = (int64_t)b * p.heads + head0;  // first output row of this workgroup
+  float* x_ml = reinterpret_cast<float*>(&sm.tile[0][0]);  // [64 heads][2]: m, l
+  float* x_z = x_ml + 2 * kHW;                               // [64 heads][8]: zero-term sums
 
   // bf16 items: the 16-byte chunks of a tile's rows (32 tokens x 72 chunks) are spread over all
   // 512 threads (chunk tid + 512 e; the fifth, e = 4, exists only for the QK threads), requested at
@@ -510,10 +518,22 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       const float l_tot = row16_sum(l_part[i]);
       if (L16 == 0) {
-        const int64_t hrow = row0 + 16 * w + 4 * G + i;
-        p.ws_ml[2 * hrow] = m_run[i];
-        p.ws_ml[2 * hrow + 1] = l_tot;
+        const int hh = 16 * w + 4 * G + i;
+        if (direct) {
+          x_ml[2 * hh] = m_run[i];
+          x_ml[2 * hh + 1] = l_tot;
+          if (p.lse)
+            p.lse[orow0 + hh] = m_run[i] == -__builtin_inff() ? -__builtin_inff()
+                                                              : (m_run[i] + __log2f(l_tot)) * 0.69314718055994531f;
+        } else {
+          p.ws_ml[2 * (row0 + hh)] = m_run[i];
+          p.ws_ml[2 * (row0 + hh) + 1] = l_tot;
+        }
       }
+    }
+    if (direct) {
+      if (tid == 0) atomicAdd(p.plan_hdr + kHdrDirect, 1);
+      __syncthreads();  // (the PV waves' matching barrier is in their epilogue)
     }
   } else {
     // ============ PV waves: content groups 2v, 2v + 1 for all 64 heads ============
@@ -639,7 +659,15 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         __syncthreads();
       }
     }
-    // unnormalised partial output and zero-term sums.  Registers 4a .. 4a + 3 of lanes l and l ^ 32
+    if (direct) {
+      if (G < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x_z[(16 * v + L16) * 8 + 4 * G + i] = oz[i];
+      }
+      __syncthreads();  // every head's max, sum and zero-term sums are in place
+    }
+    // unnormalised partial output and zero-term sums (direct: the final bf16 outputs of the head
+    // rows, (sum + zero term of the group) / sum of probabilities).  Registers 4a .. 4a + 3 of lanes l and l ^ 32
     // hold the 8 channels 8 (16 v + 4 cb + a) + 0..7 between them, in the unpacking order; each
     // lane takes two values from the other, so that the lower half holds channels 0..3 and the
     // upper half channels 4..7, written as one 16-byte store.
@@ -647,7 +675,15 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
     const float e2[2] = {__builtin_ldexpf(1.f, cur_e[0]), __builtin_ldexpf(1.f, cur_e[1])};  // undo 2^-E_g
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float* dh = p.ws_o + (row0 + 32 * hb + l32) * kDc;
+      const int hh = 32 * hb + l32;
+      float* dh = p.ws_o + (row0 + hh) * kDc;
+      uint16_t* oh = p.out + (orow0 + hh) * kDc;
+      float inv = 0.f, zg[2] = {0.f, 0.f};  // (direct) 1 / sum, zero terms of groups 2v, 2v + 1
+      if (direct) {
+        inv = x_ml[2 * hh] == -__builtin_inff() ? 0.f : 1.f / x_ml[2 * hh + 1];
+        zg[0] = x_z[hh * 8 + 2 * v];
+        zg[1] = x_z[hh * 8 + 2 * v + 1];
+      }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -664,10 +700,12 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
             const float ry = __shfl_xor(odd ? x[2] : x[3], 32, 64);
             r = odd ? f32x4{rx, ry, x[1], x[3]} : f32x4{x[0], x[2], rx, ry};
           }
-          *reinterpret_cast<f32x4*>(dh + 8 * (16 * v + 4 * cb + a) + 4 * half) = r;
+          const int c0 = 8 * (16 * v + 4 * cb + a) + 4 * half;  // channels c0 .. c0 + 3, group 2v + cb / 2
+          if (direct) store_bf16x4(oh + c0, (r + zg[cb >> 1]) * inv);
+          else *reinterpret_cast<f32x4*>(dh + c0) = r;
         }
     }
-    if (G < 2) {
+    if (G < 2 && !direct) {
       const int64_t hrow = row0 + 16 * v + L16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.ws_z[hrow * 8 + 4 * G + i] = oz[i];

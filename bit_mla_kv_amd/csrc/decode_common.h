@@ -133,5 +133,50 @@ __device__ __forceinline__ void signal(lds_vint* flag, int value, int lane) {
   if (lane == 0) *flag = value;
 }
 
+// ---- split-plan facts about sequence b, shared by the planner, the decode kernels and the combine
+__device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, int* first_page) {
+  int N = p.seq_len[b];
+  const int slot = p.seq_slot[b];
+  if (slot < 0 || slot >= p.num_slots) N = 0;
+  const int p_lo = p.n_sink, p_hi = N - p.n_recent;
+  *first_page = p_lo / kPageTokens;
+  return p_hi > p_lo ? (p_hi - 1) / kPageTokens - *first_page + 1 : 0;
+}
+// the sequence's bf16 tokens (sink, then the recent window) and their count in 64-token pages
+__device__ __forceinline__ int seq_bf16_tokens(const DecodeParams& p, int b) {
+  int N = p.seq_len[b];
+  const int slot = p.seq_slot[b];
+  if (slot < 0 || slot >= p.num_slots) N = 0;
+  return bf16_token_count(N, p.n_sink, p.n_recent);
+}
+__device__ __forceinline__ int seq_bf16_pages(const DecodeParams& p, int b) {
+  return (seq_bf16_tokens(p, b) + kPageTokens - 1) / kPageTokens;
+}
+// bf16 items of a sequence with chunks of pps pages: at least one (an empty sequence still leaves
+// a partial row for the combine)
+__device__ __forceinline__ int bf16_items(int bf_pages, int pps) { return max(1, (bf_pages + pps - 1) / pps); }
+
+// Sequence b is decoded by one work item (no packed chunk, one bf16 chunk, and that item is in the
+// list): that item's workgroups write the final outputs and lse themselves and the combine leaves
+// the sequence alone.  Read after the plan kernel has run.
+__device__ __forceinline__ bool decoded_in_one_item(const DecodeParams& p, int b) {
+  int fp;
+  return p.seq_info[4 * b + 3] >= 0 && seq_packed_pages(p, b, &fp) == 0 &&
+         bf16_items(seq_bf16_pages(p, b), p.plan_hdr[kHdrPagesPerSplit]) == 1;
+}
+
+__device__ __forceinline__ uint16_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// four outputs as bf16 (round to nearest even), one 8-byte store
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 v) {
+  uint2 q;
+  q.x = (uint32_t)f2bf_rne(v[0]) | ((uint32_t)f2bf_rne(v[1]) << 16);
+  q.y = (uint32_t)f2bf_rne(v[2]) | ((uint32_t)f2bf_rne(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = q;
+}
+
 }  // namespace dev
 }  // namespace mla

@@ -29,6 +29,7 @@ __host__ __device__ inline int bf16_token_count(int N, int n_sink, int n_recent)
 // decode call; the decode kernels add to the counters.
 constexpr int kHdrItems = 0;          // work items of this call
 constexpr int kHdrPagesPerSplit = 1;  // pages per packed chunk
+constexpr int kHdrDirect = 2;        // workgroups that wrote their sequence's final output (one-item sequences)
 constexpr int kHdrGiveUps = 4;        // handshake waits between two waves that gave up (bounded wait)
 constexpr int kHdrBadPages = 5;       // page reads whose block-table entry lay outside the table or pool
 constexpr int kHdrBadSeqs = 6;        // sequences with a slot outside the cache or a length outside [0, max_seq_len]

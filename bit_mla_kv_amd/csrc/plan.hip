@@ -11,7 +11,8 @@
 // longest-first schedule of the packed work.  When a slightly longer chunk lets
 // every packed item run at once (one round of workgroups), that chunk is used.  combine_kernel merges each
 // sequence's partial results exactly (max-shifted sums), adding the deferred
-// zero terms, and writes bf16 outputs and natural-log lse.
+// zero terms, and writes bf16 outputs and natural-log lse; a sequence decoded in
+// one work item has had its outputs written by the decode kernel and is skipped.
 #include <algorithm>
 
 #include "decode_common.h"
@@ -22,28 +23,6 @@ using namespace dev;
 
 constexpr int kPlanThreads = 64;  // one wave: scans are lane shuffles, no workgroup barriers
 constexpr int kPlanRegs = 8;      // sequence lengths a lane keeps in registers for the chunk search
-
-__device__ __forceinline__ int seq_packed_pages(const DecodeParams& p, int b, int* first_page) {
-  int N = p.seq_len[b];
-  const int slot = p.seq_slot[b];
-  if (slot < 0 || slot >= p.num_slots) N = 0;
-  const int p_lo = p.n_sink, p_hi = N - p.n_recent;
-  *first_page = p_lo / kPageTokens;
-  return p_hi > p_lo ? (p_hi - 1) / kPageTokens - *first_page + 1 : 0;
-}
-// the sequence's bf16 tokens (sink, then the recent window) and their count in 64-token pages
-__device__ __forceinline__ int seq_bf16_tokens(const DecodeParams& p, int b) {
-  int N = p.seq_len[b];
-  const int slot = p.seq_slot[b];
-  if (slot < 0 || slot >= p.num_slots) N = 0;
-  return bf16_token_count(N, p.n_sink, p.n_recent);
-}
-__device__ __forceinline__ int seq_bf16_pages(const DecodeParams& p, int b) {
-  return (seq_bf16_tokens(p, b) + kPageTokens - 1) / kPageTokens;
-}
-// bf16 items of a sequence with chunks of pps pages: at least one (an empty sequence still leaves
-// a partial row for the combine)
-__device__ __forceinline__ int bf16_items(int bf_pages, int pps) { return max(1, (bf_pages + pps - 1) / pps); }
 
 // exclusive scan over the 64 lanes of the wave; *total gets the sum
 __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
@@ -205,8 +184,9 @@ __device__ void write_counters(const DecodeParams& p, int t) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
   if (t == 0) {
-    p.plan_hdr[kHdrGiveUps] = 0;  // the decode kernels add to these two
+    p.plan_hdr[kHdrGiveUps] = 0;  // the decode kernels add to these three
     p.plan_hdr[kHdrBadPages] = 0;
+    p.plan_hdr[kHdrDirect] = 0;
     p.plan_hdr[kHdrBadSeqs] = bad;
   }
 }
@@ -289,12 +269,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   }
 }
 
-__device__ __forceinline__ uint16_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 // One workgroup of 4 waves per (sequence, head).  Wave w merges the sequence's partial rows
 // w, w + 4, ... over all 512 channels (8 per lane), eight rows at a time with every load
 // requested before use, as a running max-shifted sum; the four waves' sums are then joined
@@ -322,7 +296,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
   // the sequence's bf16 chunks are consecutive items from bi on (chunks of 64 P tokens)
   const int nbi = bi < 0 ? 0 : min(bf16_items(seq_bf16_pages(p, b), p.plan_hdr[kHdrPagesPerSplit]),
                                    min(p.plan_hdr[kHdrItems], p.max_items) - bi);
-  const int n_rows = live ? nf + (tl >= 0) + nbi : 0;
+  // a sequence decoded in one item has its outputs written by the decode kernel already
+  const bool direct = live && decoded_in_one_item(p, b);
+  const int n_rows = live && !direct ? nf + (tl >= 0) + nbi : 0;
   auto item_of = [&](int k) {
     return k < nf ? fo + k : (k == nf && tl >= 0 ? tl : bi + (k - nf - (tl >= 0)));
   };
@@ -394,7 +370,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
       acc1 = o1;
     }
   }
-  if (!live) return;
+  if (!live || direct) return;
   float L = -__builtin_inff();
   if (M != -__builtin_inff()) {
     const float inv = 1.f / den;
@@ -403,13 +379,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParam
     L = M + __log2f(den);
   }
   uint16_t* o = p.out + rid * kDc;
-  uint2 q0, q1;
-  q0.x = (uint32_t)f2bf_rne(acc0[0]) | ((uint32_t)f2bf_rne(acc0[1]) << 16);
-  q0.y = (uint32_t)f2bf_rne(acc0[2]) | ((uint32_t)f2bf_rne(acc0[3]) << 16);
-  q1.x = (uint32_t)f2bf_rne(acc1[0]) | ((uint32_t)f2bf_rne(acc1[1]) << 16);
-  q1.y = (uint32_t)f2bf_rne(acc1[2]) | ((uint32_t)f2bf_rne(acc1[3]) << 16);
-  *reinterpret_cast<uint2*>(o + 4 * lane) = q0;
-  *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = q1;
+  store_bf16x4(o + 4 * lane, acc0);
+  store_bf16x4(o + 256 + 4 * lane, acc1);
   if (p.lse && lane == 0) p.lse[rid] = L * 0.69314718055994531f;
 }
 

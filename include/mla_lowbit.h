@@ -39,7 +39,8 @@
  *    there enqueues nothing.  A decode enqueues three kernels (split plan,
  *    decode, combine); should a later launch fail after an earlier one was
  *    enqueued, the call returns MLA_LOWBIT_ERR_DEVICE with the HIP message and
- *    the enqueued kernels write only the workspace, never out or lse.
+ *    the enqueued kernels write the workspace and, of out and lse, only the
+ *    rows of sequences decoded in one work item (see mla_lowbit_decode).
  *  - Device-resident index data (block_table entries, token positions,
  *    slots, sequence lengths) is the caller's contract.  The kernels never
  *    read or write outside the buffers the structs describe: an append skips
@@ -198,7 +199,10 @@ size_t mla_lowbit_decode_workspace_bytes(const mla_lowbit_layout* layout, int32_
  * Token t of a sequence is read from its bf16 row when t < n_sink or
  * t >= N - n_recent, otherwise from its packed copy.  The work is split
  * along the context into page-aligned chunks whose partial results are
- * merged exactly with a log-sum-exp combine.
+ * merged exactly with a log-sum-exp combine.  A sequence decoded in one work
+ * item (no packed tokens and at most one chunk of bf16 tokens, e.g. every
+ * N <= n_sink + n_recent) has its out and lse rows written by the decode
+ * kernel itself, with the combine's arithmetic, and skips the combine.
  */
 int mla_lowbit_decode(const mla_lowbit_cache* cache, const void* q, const int32_t* seq_slot, const int32_t* seq_len,
                       int32_t batch, int32_t num_heads, int32_t max_seq_len, float softmax_scale, void* out,

@@ -279,6 +279,34 @@ def test_all_bf16_long_window_chunks(heads):
         assert np.max(np.abs(o - outs[0])) <= 4e-3 * np.max(np.abs(outs[0]))
 
 
+HDR_DIRECT = 2  # workspace header word: workgroups that wrote their sequence's final outputs
+
+
+@pytest.mark.parametrize("heads,bits_c", [(16, 4), (16, 2), (64, 4), (128, 2)])
+def test_one_item_sequences_written_by_the_decode(heads, bits_c):
+    """A sequence with no packed tokens and one bf16 chunk (here every N <= n_sink + n_recent, N = 0
+    included) is decoded by one work item, whose workgroups write its final bf16 outputs and lse;
+    the combine leaves it alone and merges the longer ones.  out and lse start as NaN, so a row
+    that nobody writes fails; header word 2 counts the workgroups that wrote directly."""
+    lens = [0, 1, 5, 64, 132, 133, 900, 3000]
+    rows = [mi.rows(33, b, n) for b, n in enumerate(lens)]
+    cache = build(rows, bits_c, seed=33)
+    B, dev = len(lens), cache.pages.device
+    q = mi.queries(33, B, heads)
+    qd = cb.to_device_bf16(q.reshape(B * heads, -1), dev).view(B, heads, 576)
+    out = torch.full((B, heads, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, heads), float("nan"), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(cache.layout, B, heads, max(lens), dev)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    m.decode(cache, qd, slots, torch.tensor(lens, dtype=torch.int32, device=dev), max(lens), SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = reference(rows, q, bits_c, SCALE)
+    check(out, lse, ref_o, ref_l, f"one-item H{heads} C{bits_c}")
+    workgroups_per_item = heads // 64 if heads % 64 == 0 else heads // 16
+    n_direct = sum(n <= 132 for n in lens)
+    assert int(ws[:32].view(torch.int32)[HDR_DIRECT].item()) == n_direct * workgroups_per_item
+
+
 def run_decode_multi(cache, q_u16, lens, max_len=None):
     """q_u16 [B, q_len, H, 576] -> (out [B, q_len, H, 512], lse [B, q_len, H])."""
     B, QL, H = q_u16.shape[:3]
