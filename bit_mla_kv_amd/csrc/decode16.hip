@@ -425,8 +425,11 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
     __syncthreads();  // the prologue area is read; the buffers overlay it from here on
 
     float m_run[4], l_part[4];  // heads 4G + i
+    float m_thr[4], m_sub[4];   // m_run + kRescale, and m_run as subtracted from scores (0 while -inf)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      m_thr[i] = -__builtin_inff();
+      m_sub[i] = 0.f;
       m_run[i] = -__builtin_inff();
       l_part[i] = 0.f;
     }
@@ -466,7 +469,7 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
         const int tok = tok0 + 16 * h + L16;
         valid[h] = tok >= it.p_lo && tok < it.p_hi;
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) mw[h][g] = valid[h] ? R.m[h][g] : 0u;
+        for (int g = 0; g < kGroups; ++g) mw[h][g] = R.m[h][g];  // (invalid tokens: masked below)
         uint32_t kr[4];
         nib_bytes(R.r[h].x, kr[0], kr[1]);
         nib_bytes(R.r[h].y, kr[2], kr[3]);
@@ -498,13 +501,16 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
         for (int g = 0; g < 8; ++g) zlo[g] = (f16)bf16f(mw[h][g] >> 16);
         const f16 z8 = (f16)bf16f(mw[h][8] >> 16);
         const f16x8 zf = G < 2 ? zlo : f16x8{z8, 0, 0, 0, 0, 0, 0, 0};
-        S[h] = mfma32k_acc(qz, zf, acc[h] * hs) + (valid[h] ? 0.f : -__builtin_inff());
+        // an invalid token's score is -inf whatever its (possibly unwritten) metadata held
+        const f32x4 sc = mfma32k_acc(qz, zf, acc[h] * hs);
+        const float ninf = -__builtin_inff();
+        S[h] = valid[h] ? sc : f32x4{ninf, ninf, ninf, ninf};
       }
       // online softmax: a head's running max is refreshed only when one of its scores exceeds it
       // by more than kRescale
       bool need = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) need |= (S[0][i] > m_run[i] + kRescale) | (S[1][i] > m_run[i] + kRescale);
+      for (int i = 0; i < 4; ++i) need |= (S[0][i] > m_thr[i]) | (S[1][i] > m_thr[i]);
       const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
       if (any) {
         f32x4 alpha;
@@ -513,6 +519,8 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
           const float m_new = fmaxf(m_run[i], row16_max(fmaxf(S[0][i], S[1][i])));
           alpha[i] = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
           m_run[i] = m_new;
+          m_thr[i] = m_new + kRescale;
+          m_sub[i] = m_new == -__builtin_inff() ? 0.f : m_new;
           l_part[i] *= alpha[i];
         }
         if (L16 == 0) *reinterpret_cast<f32x4*>(&B.alpha[4 * G]) = alpha;
@@ -522,8 +530,7 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
         f16x4 pz;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float mu = m_run[i] == -__builtin_inff() ? 0.f : m_run[i];
-          const float e = __builtin_amdgcn_exp2f(S[h][i] - mu);
+          const float e = __builtin_amdgcn_exp2f(S[h][i] - m_sub[i]);
           l_part[i] += e;
           pz[i] = (f16)e;
         }
@@ -543,6 +550,7 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
           v = G == 1 ? mw[h][2 + q] : v;
           v = G == 2 ? mw[h][4 + q] : v;
           v = G == 3 ? mw[h][6 + q] : v;
+          v = valid[h] ? v : 0u;  // an invalid token gets PV scale and zero 0
           mq[h][q] = v;
           sg[h][q] = bf16f(v & 0xFFFFu);
         }
