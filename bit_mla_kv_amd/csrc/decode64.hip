@@ -364,8 +364,11 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       }
     };
     float m_run[4], l_part[4];  // heads .. + 4G + i (the lane's D rows)
+    float m_thr[4], m_sub[4];   // m_run + kRescale, and m_run as subtracted from scores (0 while -inf)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      m_thr[i] = -__builtin_inff();
+      m_sub[i] = 0.f;
       m_run[i] = -__builtin_inff();
       l_part[i] = 0.f;
     }
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       // exceeds it by more than kRescale
       bool need = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) need |= (S[0][i] > m_run[i] + kRescale) | (S[1][i] > m_run[i] + kRescale);
+      for (int i = 0; i < 4; ++i) need |= (S[0][i] > m_thr[i]) | (S[1][i] > m_thr[i]);
       const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
       float alpha[4] = {1.f, 1.f, 1.f, 1.f};
       if (any) {
@@ -448,15 +451,16 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           const float m_new = fmaxf(m_run[i], mx);
           alpha[i] = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
           m_run[i] = m_new;
+          m_thr[i] = m_new + kRescale;
+          m_sub[i] = m_new == -__builtin_inff() ? 0.f : m_new;
           l_part[i] *= alpha[i];
         }
       }
       f16x4 pz[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float mu = m_run[i] == -__builtin_inff() ? 0.f : m_run[i];
-        const float e0 = __builtin_amdgcn_exp2f(S[0][i] - mu);
-        const float e1 = __builtin_amdgcn_exp2f(S[1][i] - mu);
+        const float e0 = __builtin_amdgcn_exp2f(S[0][i] - m_sub[i]);
+        const float e1 = __builtin_amdgcn_exp2f(S[1][i] - m_sub[i]);
         l_part[i] += e0 + e1;
         pz[0][i] = (f16)e0;
         pz[1][i] = (f16)e1;
