@@ -116,7 +116,6 @@ struct __align__(16) Smem64 {
   f16 tile[kSlots][kT * kS];       // exact codes of a tile's tokens + zero-term columns
   f16 probT[2][kT][kPT];           // fp16 probabilities [token][head] of steps k (QK) and k - 1 (PV)
   float sq[kSlots][kGroups][kT];   // s_g * scale * log2 e at sq_pos(token); 0 for masked tokens
-  float bias[kSlots][kT];          // at sq_pos(token): 0 valid, -inf masked
   f16 svh[kSlots][8][kT];          // PV group scale s_g * 2^-E_g (fp16); 0 for masked tokens
   float alpha[2][kHW];             // per-head rescale factor for the PV accumulators
   int resc[2][4];                  // per-QK-wave flags: bit 0 some head was rescaled, bit 1 the wave's
@@ -283,9 +282,10 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           for (int g = 0; g < kGroups; ++g) sm.sq[sl][g][sq_pos(r)] = valid ? c_log2 : 0.f;
 #pragma unroll
           for (int g = 0; g < 8; ++g) sm.svh[sl][g][r] = valid ? (f16)1.f : (f16)0.f;
-          sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
           *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) = make_uint4(0, 0, 0, 0);
+          const f16 mask = valid ? (f16)0.f : (f16)(-__builtin_inff());
+          *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
+              make_uint4(__builtin_bit_cast(uint32_t, f16x2{(f16)0.f, mask}), 0, 0, 0);
         }
         return;
       }
@@ -318,14 +318,14 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
         sm.svh[sl][g][r] = (f16)(sc * pv_inv);
         tile[r * kS + kZ + g] = (f16)(valid ? bf16f(R.m[0] >> 16) : 0.f);
-        if (g == 0) sm.bias[sl][sq_pos(r)] = valid ? 0.f : -__builtin_inff();
       }
       if (ft < kT) {
         const float sc = valid ? bf16f(R.m[1] & 0xFFFFu) : 0.f;
         sm.sq[sl][8][sq_pos(r)] = sc * c_log2;
         const f16 z8 = (f16)(valid ? bf16f(R.m[1] >> 16) : 0.f);
+        const f16 mask = valid ? (f16)0.f : (f16)(-__builtin_inff());  // score mask, column kZ + 9
         *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
-            make_uint4(__builtin_bit_cast(uint32_t, f16x2{z8, (f16)0.f}), 0, 0, 0);
+            make_uint4(__builtin_bit_cast(uint32_t, f16x2{z8, mask}), 0, 0, 0);
       }
     };
 
@@ -354,13 +354,14 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         qs[g] *= c_log2;
       }
       // zero-term step, k = 8 G + j: G0 hi(qsum_j), G1 lo(qsum_j) against z_j; G2 / G3 hi / lo of
-      // qsum_8 in slot j = 0 against z_8 (the other slots meet zero columns)
+      // qsum_8 in slot j = 0 against z_8, and 1 in slot j = 1 against the token's score mask (0, or
+      // -inf for a token outside the item: twice -inf is -inf); the other slots meet zero columns
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x = G < 2 ? qs[j] : (j == 0 ? qs[8] : 0.f);
         const f16 hi = (f16)x;
         const f16 lo = (f16)(x - (float)hi);
-        qz[j] = (G & 1) ? lo : hi;
+        qz[j] = G >= 2 && j == 1 ? (f16)1.f : (G & 1) ? lo : hi;
       }
     };
     float m_run[4], l_part[4];  // heads .. + 4G + i (the lane's D rows)
@@ -421,10 +422,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         const int zc = kZ + 8 * (G >> 1);
         const f16x8 zr0 = lds_load<f16x8>(tb + L16 * kS + zc);
         const f16x8 zr1 = lds_load<f16x8>(tb + (16 + L16) * kS + zc);
-        const f32x2 bv = lds_load<f32x2>(lds_opaque(&sm.bias[sl][0]) + 2 * L16);
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        S[0] = s[0] + mfma16(qz, zr0, z4) + bv[0];
-        S[1] = s[1] + mfma16(qz, zr1, z4) + bv[1];
+        S[0] = mfma16(qz, zr0, s[0]);
+        S[1] = mfma16(qz, zr1, s[1]);
       }
       if (!packed && p.q_len > 1) {
         // several query tokens: this wave's query (its 16 heads belong to one) sees the first
