@@ -285,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = make_uint4(0, 0, 0, 0);
           const f16 mask = valid ? (f16)0.f : (f16)(-__builtin_inff());
           *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
-              make_uint4(__builtin_bit_cast(uint32_t, f16x2{(f16)0.f, mask}), 0, 0, 0);
+              make_uint4(__builtin_bit_cast(uint32_t, f16x2{(f16)0.f, mask}),
+                         __builtin_bit_cast(uint32_t, f16x2{(f16)1.f, (f16)0.f}), 0, 0);
         }
         return;
       }
@@ -324,8 +325,10 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         sm.sq[sl][8][sq_pos(r)] = sc * c_log2;
         const f16 z8 = (f16)(valid ? bf16f(R.m[1] >> 16) : 0.f);
         const f16 mask = valid ? (f16)0.f : (f16)(-__builtin_inff());  // score mask, column kZ + 9
+        // column kZ + 10 holds 1: the PV waves' zero-term MFMA sums each head's probabilities there
         *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
-            make_uint4(__builtin_bit_cast(uint32_t, f16x2{z8, mask}), 0, 0, 0);
+            make_uint4(__builtin_bit_cast(uint32_t, f16x2{z8, mask}),
+                       __builtin_bit_cast(uint32_t, f16x2{(f16)1.f, (f16)0.f}), 0, 0);
       }
     };
 
@@ -364,14 +367,13 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         qz[j] = G >= 2 && j == 1 ? (f16)1.f : (G & 1) ? lo : hi;
       }
     };
-    float m_run[4], l_part[4];  // heads .. + 4G + i (the lane's D rows)
+    float m_run[4];  // heads .. + 4G + i (the lane's D rows)
     float m_thr[4], m_sub[4];   // m_run + kRescale, and m_run as subtracted from scores (0 while -inf)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m_thr[i] = -__builtin_inff();
       m_sub[i] = 0.f;
       m_run[i] = -__builtin_inff();
-      l_part[i] = 0.f;
     }
     // QK and softmax of tile k; probabilities to probT[k % 2]
     auto qk_step = [&](int k) {
@@ -452,7 +454,6 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           m_run[i] = m_new;
           m_thr[i] = m_new + kRescale;
           m_sub[i] = m_new == -__builtin_inff() ? 0.f : m_new;
-          l_part[i] *= alpha[i];
         }
       }
       f16x4 pz[2];
@@ -460,7 +461,6 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       for (int i = 0; i < 4; ++i) {
         const float e0 = __builtin_amdgcn_exp2f(S[0][i] - m_sub[i]);
         const float e1 = __builtin_amdgcn_exp2f(S[1][i] - m_sub[i]);
-        l_part[i] += e0 + e1;
         pz[0][i] = (f16)e0;
         pz[1][i] = (f16)e1;
       }
@@ -516,22 +516,13 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         __syncthreads();
       }
     }
-    // running max and sum of the heads of this wave
+    // running max of the heads of this wave (their sums come from the PV waves)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float l_tot = row16_sum(l_part[i]);
       if (L16 == 0) {
         const int hh = 16 * w + 4 * G + i;
-        if (direct) {
-          x_ml[2 * hh] = m_run[i];
-          x_ml[2 * hh + 1] = l_tot;
-          if (p.lse)
-            p.lse[orow0 + hh] = m_run[i] == -__builtin_inff() ? -__builtin_inff()
-                                                              : (m_run[i] + __log2f(l_tot)) * 0.69314718055994531f;
-        } else {
-          p.ws_ml[2 * (row0 + hh)] = m_run[i];
-          p.ws_ml[2 * (row0 + hh) + 1] = l_tot;
-        }
+        if (direct) x_ml[2 * hh] = m_run[i];
+        else p.ws_ml[2 * (row0 + hh)] = m_run[i];
       }
     }
     if (direct) {
@@ -541,7 +532,9 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
   } else {
     // ============ PV waves: content groups 2v, 2v + 1 for all 64 heads ============
     const int v = w - 4;
-    f32x4 oz = {0.f, 0.f, 0.f, 0.f};  // rows z index 4G + i, column head 16v + L16: sum_t p z
+    // rows z index 4G + i, column head 16v + L16: sum_t p z_i for i < 8; row 10 (G = 2, register 2)
+    // meets the ones column: the head's sum of probabilities
+    f32x4 oz = {0.f, 0.f, 0.f, 0.f};
     f32x16 O[2][4];                    // [head block][channel block]
     int cur_e[2] = {0, 0};             // O[.][2 gi + c] holds sum_t code * p * s * 2^-cur_e[gi]
 #pragma unroll
@@ -667,7 +660,15 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x_z[(16 * v + L16) * 8 + 4 * G + i] = oz[i];
       }
+      if (G == 2) x_ml[2 * (16 * v + L16) + 1] = oz[2];
       __syncthreads();  // every head's max, sum and zero-term sums are in place
+      if (G == 2 && p.lse) {
+        const float mh = x_ml[2 * (16 * v + L16)];
+        p.lse[orow0 + 16 * v + L16] =
+            mh == -__builtin_inff() ? -__builtin_inff() : (mh + __log2f(oz[2])) * 0.69314718055994531f;
+      }
+    } else if (G == 2) {
+      p.ws_ml[2 * (row0 + 16 * v + L16) + 1] = oz[2];
     }
     // unnormalised partial output and zero-term sums (direct: the final bf16 outputs of the head
     // rows, (sum + zero term of the group) / sum of probabilities).  Registers 4a .. 4a + 3 of lanes l and l ^ 32
