@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
 
     if (packed) {
       // the PV threads load and unpack the content dwords the QK threads leave (same three-tile
-      // register ring: step k requests tile k + 3, accumulates tile k - 1, unpacks tile k + 1)
+      // register ring: step k requests tile k + 3, unpacks tile k + 1, accumulates tile k - 1)
       const int pt = tid - 256;
       cint* bt = (cint*)(uintptr_t)(p.block_table + (int64_t)slot * p.max_pages);
       auto pload = [&](int t, PVRegs<BITS_C>& R) {
@@ -627,8 +627,10 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
       };
       auto step = [&](int k, PVRegs<BITS_C>& next, const PVRegs<BITS_C>& cur) {
         pload(k + 3, next);
-        pv_step(k);
+        // the unpack first: its VALU work meets the QK waves' MFMAs at the start of the step, and
+        // the PV MFMAs meet the QK waves' softmax and unpack at its end
         if (k + 1 < n_tiles) pfill(k + 1, cur);
+        pv_step(k);
         __syncthreads();
       };
       PVRegs<BITS_C> R0, R1, R2;
