@@ -19,8 +19,7 @@
 //    into registers and unpack the next tile into an fp16 tile of exact codes
 //    (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
 //    converted with a 2^9 scale) plus per-token scales, zeros and masks; they
-//    take 3/8 of the content codes (1/4 at 2 bits), the RoPE-key codes and the
-//    metadata;
+//    take a quarter of the content codes, the RoPE-key codes and the metadata;
 //  - PV waves 4..7 hold the output of content groups 2v, 2v+1 (v = w - 4) for
 //    all 64 heads and accumulate p * s_g times the exact codes (MFMA 32x32x16
 //    f16, both operands read with the LDS transpose load) plus the zero-term
@@ -62,7 +61,7 @@ struct Geo {
   static constexpr int CDW = kT * CB / 4;      // content dwords of a tile
   static constexpr int DPR = CB / 4;           // content dwords per token
   static constexpr int CPT = CDW / 256;        // content dwords per thread index (QK and PV threads share them)
-  static constexpr int CQ = CPT / 2 - 1;       // content dwords a QK thread unpacks; a PV thread takes the rest
+  static constexpr int CQ = CPT / 4;           // content dwords a QK thread unpacks; a PV thread takes the rest
   static constexpr int RPT = kT * kDr / 8 / 256;  // RoPE dwords per unpack thread (1)
   static_assert(CDW % 256 == 0 && RPT == 1, "unpack split assumes these sizes");
 };
