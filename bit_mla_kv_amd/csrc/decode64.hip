@@ -13,8 +13,11 @@
 //    lane owns one token of a 16-token block and applies that token's fp32
 //    group scales as scalars).  The zero terms of all nine groups go through
 //    one more MFMA against the tile's zero columns with qsum split into fp16
-//    hi + lo.  Online softmax in the log2 domain with a lazily refreshed
-//    running max; probabilities are published to LDS as fp16 [token][head].
+//    hi + lo; it also adds each token's score mask (0, or -inf for a token
+//    outside the item) and takes the group-scaled sum as its accumulator, so
+//    the score leaves it complete.  Online softmax in the log2 domain with a
+//    lazily refreshed running max; probabilities are published to LDS as fp16
+//    [token][head].
 //    The same waves also load the packed bytes of the tile three steps ahead
 //    into registers and unpack the next tile into an fp16 tile of exact codes
 //    (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
@@ -27,11 +30,14 @@
 //    probabilities.  They load and unpack the rest of the content codes, so
 //    both roles of a SIMD share the unpacking work (the split that measured
 //    fastest: the QK waves carry the softmax and the metadata).
-// Tiles flow through a three-slot LDS ring: in step k the QK waves score tile
-// k and write tile k + 1, the PV waves accumulate tile k - 1; one workgroup
-// barrier per tile.
+// Tiles flow through a three-slot LDS ring, one workgroup barrier per tile: in
+// step k the QK waves score tile k (MFMAs first, then the softmax and their
+// share of the unpacking of tile k + 1) and the PV waves accumulate tile k - 1
+// (their unpacking first, then the MFMAs), so that each role's VALU work meets
+// the other's MFMAs on the shared SIMD.
 // Partials are left unnormalised with their running max and sum; the combine
-// kernel adds the zero terms and merges splits.
+// kernel adds the zero terms and merges splits.  A sequence decoded in one item
+// gets its final outputs and lse here instead.
 #include <algorithm>
 #include <type_traits>
 
