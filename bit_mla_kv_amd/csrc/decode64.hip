@@ -54,7 +54,7 @@ constexpr int kHW = 64;           // query heads per workgroup
 constexpr int kThreads = 512;     // 4 QK + unpack waves, 4 PV waves
 constexpr int kSlots = 3;         // tile ring
 constexpr int kS = 592;           // tile row stride (halves): 576 codes + 16 zero-term columns
-constexpr int kZ = 576;           // zero-term columns: z_0..z_7, then z_8 and seven zeros
+constexpr int kZ = 576;           // zero-term columns: z_0..z_7, z_8, the score mask, 1, five zeros
 constexpr int kPT = 72;           // probability row stride (halves); rows are tokens
 constexpr float kRescale = 8.0f;  // lazy max refresh threshold, log2 units
 
