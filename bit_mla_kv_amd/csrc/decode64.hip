@@ -55,7 +55,7 @@ constexpr int kThreads = 512;     // 4 QK + unpack waves, 4 PV waves
 constexpr int kSlots = 3;         // tile ring
 constexpr int kS = 592;           // tile row stride (halves): 576 codes + 16 zero-term columns
 constexpr int kZ = 576;           // zero-term columns: z_0..z_7, z_8, the score mask, 1, five zeros
-constexpr int kPT = 72;           // probability row stride (halves); rows are tokens
+constexpr int kPT = 80;           // probability row stride (halves); rows are tokens
 constexpr float kRescale = 8.0f;  // lazy max refresh threshold, log2 units
 
 template <int BITS_C>
@@ -124,7 +124,7 @@ struct __align__(16) Smem64 {
   f16 tile[kSlots][kT * kS];       // exact codes of a tile's tokens + zero-term columns
   f16 probT[2][kT][kPT];           // fp16 probabilities [token][head] of steps k (QK) and k - 1 (PV)
   float sq[kSlots][kGroups][kT];   // s_g * scale * log2 e at sq_pos(token); 0 for masked tokens
-  f16 svh[kSlots][8][kT];          // PV group scale s_g * 2^-E_g (fp16); 0 for masked tokens
+  f16 svh[kSlots][8][kT];          // PV group scale s_g * 2^-E_g (fp16) at pv_pos(token); 0 for masked tokens
   float alpha[2][kHW];             // per-head rescale factor for the PV accumulators
   int resc[2][4];                  // per-QK-wave flags: bit 0 some head was rescaled, bit 1 the wave's
                                    // groups changed their PV scale exponent
@@ -134,6 +134,12 @@ struct __align__(16) Smem64 {
 // Per-token QK constants sit so that one 8-byte read gives a lane the values of its token in
 // both 16-token blocks: token r at 2 * (r % 16) + r / 16.
 __device__ __forceinline__ int sq_pos(int r) { return 2 * (r & 15) + (r >> 4); }
+
+// The PV waves' transposed reads of a tile take, per 32-lane half, the four token rows
+// 16 ks + h + 2j (j < 4) and the four 8 rows on: with row strides of 296 and 40 dwords those rows
+// fall on distinct LDS banks (consecutive rows would not).  The PV scale of token r sits at
+// pv_pos(r) so that one 16-byte read gives the eight of (ks, h) in register order.
+__device__ __forceinline__ int pv_pos(int r) { return (r & 16) + 8 * (r & 1) + ((r & 15) >> 1); }
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
 #pragma unroll
           for (int g = 0; g < kGroups; ++g) sm.sq[sl][g][sq_pos(r)] = valid ? c_log2 : 0.f;
 #pragma unroll
-          for (int g = 0; g < 8; ++g) sm.svh[sl][g][r] = valid ? (f16)1.f : (f16)0.f;
+          for (int g = 0; g < 8; ++g) sm.svh[sl][g][pv_pos(r)] = valid ? (f16)1.f : (f16)0.f;
           *reinterpret_cast<uint4*>(&tile[r * kS + kZ]) = make_uint4(0, 0, 0, 0);
           const f16 mask = valid ? (f16)0.f : (f16)(-__builtin_inff());
           *reinterpret_cast<uint4*>(&tile[r * kS + kZ + 8]) =
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           echg = 2;
         }
         sm.sq[sl][g][sq_pos(r)] = sc * c_log2;
-        sm.svh[sl][g][r] = (f16)(sc * pv_inv);
+        sm.svh[sl][g][pv_pos(r)] = (f16)(sc * pv_inv);
         tile[r * kS + kZ + g] = (f16)(valid ? bf16f(R.m[0] >> 16) : 0.f);
       }
       if (ft < kT) {
@@ -567,8 +573,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         f16x8 A[2][4], P[2][2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int t0 = 16 * ks + 4 * half;  // k slots: tokens t0 + j (j < 4), t0 + 8 + (j - 4)
-          const int rsel = t0 + ((lane & 15) >> 2), csel = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          // k slots of this half: tokens 16 ks + half + 2j, then the same + 8 (j < 4)
+          const int rsel = 16 * ks + half + 2 * ((lane & 15) >> 2), csel = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
           const lds_ptr<f16> va = tb + rsel * kS + 128 * v + csel;
           const lds_ptr<f16> pbp = ptb + rsel * kPT + csel;
 #pragma unroll
@@ -601,8 +607,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
-            const int t0 = 16 * ks + 4 * half;
-            const f16x8 sv = cat(lds_load<f16x4>(svw + gi * kT + t0), lds_load<f16x4>(svw + gi * kT + t0 + 8));
+            const f16x8 sv = lds_load<f16x8>(svw + gi * kT + 16 * ks + 8 * half);
             const f16x8 b0 = P[ks][0] * sv, b1 = P[ks][1] * sv;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
