@@ -55,7 +55,7 @@ constexpr int kThreads = 512;     // 4 QK + unpack waves, 4 PV waves
 constexpr int kSlots = 3;         // tile ring
 constexpr int kS = 592;           // tile row stride (halves): 576 codes + 16 zero-term columns
 constexpr int kZ = 576;           // zero-term columns: z_0..z_7, z_8, the score mask, 1, five zeros
-constexpr int kPT = 80;           // probability row stride (halves); rows are tokens
+constexpr int kPT = 68;           // probability row stride (halves); row p_row(t) holds token t
 constexpr float kRescale = 8.0f;  // lazy max refresh threshold, log2 units
 
 template <int BITS_C>
@@ -135,11 +135,32 @@ struct __align__(16) Smem64 {
 // both 16-token blocks: token r at 2 * (r % 16) + r / 16.
 __device__ __forceinline__ int sq_pos(int r) { return 2 * (r & 15) + (r >> 4); }
 
-// The PV waves' transposed reads of a tile take, per 32-lane half, the four token rows
-// 16 ks + h + 2j (j < 4) and the four 8 rows on: with row strides of 296 and 40 dwords those rows
-// fall on distinct LDS banks (consecutive rows would not).  The PV scale of token r sits at
-// pv_pos(r) so that one 16-byte read gives the eight of (ks, h) in register order.
-__device__ __forceinline__ int pv_pos(int r) { return (r & 16) + 8 * (r & 1) + ((r & 15) >> 1); }
+// LDS bank placement of the probabilities and the PV operand reads.  The token order of an MFMA's
+// k slots is free, so it is chosen for the banks (as measured on gfx950: 16-byte reads go in four
+// passes of 16 lanes over 64 banks, 8-byte and transposed reads in two passes of 32 lanes over 64
+// banks, 8-byte writes in four passes of 16 lanes over 32 banks).  Token t = 16h + 8a + 4c + 2d + e
+// (one bit each):
+//  - its probabilities sit in row p_row(t) = 16h + 8d + 4e + 2(c^h) + a: with a row stride of 34
+//    dwords the QK wave's two 8-byte writes (tokens L16 and 16 + L16) cover all 32 banks per pass;
+//  - a PV read pass takes the four tokens of set x (x = ks + 2 rd + 4 half; a = x & 1,
+//    c^h = (x >> 1) & 1, e = x >> 2, slot j = d + 2h): their tile rows (stride 296 dwords) and
+//    probability rows fall on four distinct 16-bank windows each;
+//  - the zero-term reads take the eight tokens of sets x and x + 4 per pass, distinct 8-bank
+//    windows in both buffers;
+//  - its PV scale sits at pv_pos(t), so that the eight scales of (ks, half) are one 16-byte read in
+//    register order (rd = 0 then rd = 1).
+__device__ __forceinline__ int p_row(int t) {
+  const int h = (t >> 4) & 1, a = (t >> 3) & 1, c = (t >> 2) & 1, d = (t >> 1) & 1, e = t & 1;
+  return 16 * h + 8 * d + 4 * e + 2 * (c ^ h) + a;
+}
+__device__ __forceinline__ int pv_token(int x, int j) {
+  const int d = j & 1, h = j >> 1;
+  return 16 * h + 8 * (x & 1) + 4 * (((x >> 1) & 1) ^ h) + 2 * d + (x >> 2);
+}
+__device__ __forceinline__ int pv_pos(int t) {
+  const int h = (t >> 4) & 1, a = (t >> 3) & 1, c = (t >> 2) & 1, d = (t >> 1) & 1, e = t & 1;
+  return 16 * a + 8 * e + 4 * (c ^ h) + 2 * h + d;
+}
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -370,15 +391,17 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         qs[g] += __shfl_xor(qs[g], 32, 64);
         qs[g] *= c_log2;
       }
-      // zero-term step, k = 8 G + j: G0 hi(qsum_j), G1 lo(qsum_j) against z_j; G2 / G3 hi / lo of
+      // zero-term step, k = 8 G + j: G0 hi(qsum_j), G2 lo(qsum_j) against z_j; G1 / G3 hi / lo of
       // qsum_8 in slot j = 0 against z_8, and 1 in slot j = 1 against the token's score mask (0, or
-      // -inf for a token outside the item: twice -inf is -inf); the other slots meet zero columns
+      // -inf for a token outside the item: twice -inf is -inf); the other slots meet zero columns.
+      // (Lane groups 0 and 1 share LDS read passes: reading different column blocks keeps them on
+      // distinct banks.)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = G < 2 ? qs[j] : (j == 0 ? qs[8] : 0.f);
+        const float x = (G & 1) == 0 ? qs[j] : (j == 0 ? qs[8] : 0.f);
         const f16 hi = (f16)x;
         const f16 lo = (f16)(x - (float)hi);
-        qz[j] = G >= 2 && j == 1 ? (f16)1.f : (G & 1) ? lo : hi;
+        qz[j] = (G & 1) && j == 1 ? (f16)1.f : (G >> 1) ? lo : hi;
       }
     };
     float m_run[4];  // heads .. + 4G + i (the lane's D rows)
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
           s[1] += sc[1] * c1;
         }
         // zero terms of all nine groups
-        const int zc = kZ + 8 * (G >> 1);
+        const int zc = kZ + 8 * (G & 1);
         const f16x8 zr0 = lds_load<f16x8>(tb + L16 * kS + zc);
         const f16x8 zr1 = lds_load<f16x8>(tb + (16 + L16) * kS + zc);
         S[0] = mfma16(qz, zr0, s[0]);
@@ -479,9 +502,8 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         pz[1][i] = (f16)e1;
       }
       const int hc = 16 * w + 4 * G;  // first head column of the lane's rows
-      f16* prow = &sm.probT[pb][L16][hc];
-      *reinterpret_cast<f16x4*>(prow) = pz[0];
-      *reinterpret_cast<f16x4*>(prow + 16 * kPT) = pz[1];
+      *reinterpret_cast<f16x4*>(&sm.probT[pb][p_row(L16)][hc]) = pz[0];
+      *reinterpret_cast<f16x4*>(&sm.probT[pb][p_row(16 + L16)][hc]) = pz[1];
       if (L16 == 0) *reinterpret_cast<f32x4*>(&sm.alpha[pb][hc]) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
       if (lane == 0) sm.resc[pb][w] = (any ? 1 : 0) | echg;  // echg: set by the fill of tile k
     };
@@ -564,23 +586,23 @@ __global__ __launch_bounds__(kThreads) void decode64_kernel(DecodeParams p) {
         const lds_ptr<f16> ptb = lds_opaque(&sm.probT[pb][0][0]);
         // request every operand of the step before multiplying (the fence keeps them together)
         // zero-term sums for heads 16v + L16 (A: z rows from the zero-term columns, k: tokens
-        // 4G + j | 16 + 4G + j; B: the same tokens' probabilities)
-        const lds_ptr<f16> za = tb + (4 * G + (L16 >> 2)) * kS + kZ + 4 * (L16 & 3);
-        const lds_ptr<f16> pa = ptb + (4 * G + (L16 >> 2)) * kPT + 16 * v + 4 * (L16 & 3);
-        const f16x8 zA = cat(lds_tr4(za), lds_tr4(za + 16 * kS));
-        const f16x8 zP = cat(lds_tr4(pa), lds_tr4(pa + 16 * kPT));
+        // zt0 | zt1; B: the same tokens' probabilities)
+        const int zt0 = pv_token((G >> 1) + 4 * (G & 1), L16 >> 2), zt1 = pv_token((G >> 1) + 2 + 4 * (G & 1), L16 >> 2);
+        const lds_ptr<f16> za = tb + kZ + 4 * (L16 & 3), pa = ptb + 16 * v + 4 * (L16 & 3);
+        const f16x8 zA = cat(lds_tr4(za + zt0 * kS), lds_tr4(za + zt1 * kS));
+        const f16x8 zP = cat(lds_tr4(pa + p_row(zt0) * kPT), lds_tr4(pa + p_row(zt1) * kPT));
         const lds_ptr<f16> svw = lds_opaque(&sm.svh[sl][2 * v][0]);
         f16x8 A[2][4], P[2][2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          // k slots of this half: tokens 16 ks + half + 2j, then the same + 8 (j < 4)
-          const int rsel = 16 * ks + half + 2 * ((lane & 15) >> 2), csel = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const lds_ptr<f16> va = tb + rsel * kS + 128 * v + csel;
-          const lds_ptr<f16> pbp = ptb + rsel * kPT + csel;
+          // k slots of this half: the tokens of sets ks + 4 half, then ks + 2 + 4 half
+          const int t0 = pv_token(ks + 4 * half, (lane & 15) >> 2), t1 = pv_token(ks + 2 + 4 * half, (lane & 15) >> 2);
+          const int csel = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          const lds_ptr<f16> va = tb + 128 * v + csel, pbp = ptb + csel;
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) A[ks][cb] = cat(lds_tr4(va + 32 * cb), lds_tr4(va + 8 * kS + 32 * cb));
+          for (int cb = 0; cb < 4; ++cb) A[ks][cb] = cat(lds_tr4(va + t0 * kS + 32 * cb), lds_tr4(va + t1 * kS + 32 * cb));
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb) P[ks][hb] = cat(lds_tr4(pbp + 32 * hb), lds_tr4(pbp + 8 * kPT + 32 * hb));
+          for (int hb = 0; hb < 2; ++hb) P[ks][hb] = cat(lds_tr4(pbp + p_row(t0) * kPT + 32 * hb), lds_tr4(pbp + p_row(t1) * kPT + 32 * hb));
         }
         // the refresh flags are read with the operands, so one wait covers both
         if (rf[0] | rf[1] | rf[2] | rf[3]) {
