@@ -21,20 +21,72 @@ namespace mla {
 namespace {
 using namespace dev;
 
-constexpr int kPlanThreads = 64;  // one wave: scans are lane shuffles, no workgroup barriers
+constexpr int kPlanThreads = 64;  // one wave: scans are DPP row operations, no workgroup barriers
 constexpr int kPlanRegs = 8;      // sequence lengths a lane keeps in registers for the chunk search
 
+// Cross-lane scans and sums of the plan wave with DPP row operations (plain VALU instructions; a
+// ds_bpermute shuffle costs an LDS round trip, and the plan is a chain of such steps).  Inclusive
+// scan in lane order: shifts by 1, 2, 4, 8 within each 16-lane row, then the last lane of rows 0
+// and 2 into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31).  Lanes a
+// shift leaves without a source, and rows outside the row mask, take the identity (old value).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_in(int x, int identity) {
+  return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ long long dpp_in(long long x, long long identity) {
+  const int lo = __builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(identity >> 32), (int)(x >> 32), CTRL, ROW_MASK, 0xf, false);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_inclusive(T x, T identity, Op op) {
+  x = op(x, dpp_in<0x111, 0xf>(x, identity));  // row_shr:1
+  x = op(x, dpp_in<0x112, 0xf>(x, identity));  // row_shr:2
+  x = op(x, dpp_in<0x114, 0xf>(x, identity));  // row_shr:4
+  x = op(x, dpp_in<0x118, 0xf>(x, identity));  // row_shr:8
+  x = op(x, dpp_in<0x142, 0xa>(x, identity));  // row_bcast:15 into rows 1, 3
+  x = op(x, dpp_in<0x143, 0xc>(x, identity));  // row_bcast:31 into rows 2, 3
+  return x;
+}
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+__device__ __forceinline__ long long lane63(long long x) {
+  const int lo = __builtin_amdgcn_readlane((int)x, 63), hi = __builtin_amdgcn_readlane((int)(x >> 32), 63);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  return lane63(wave_inclusive(v, T(0), [](T a, T b) { return a + b; }));
+}
+__device__ __forceinline__ int wave_max(int v, int identity) {
+  return lane63(wave_inclusive(v, identity, [](int a, int b) { return max(a, b); }));
+}
 // exclusive scan over the 64 lanes of the wave; *total gets the sum
 __device__ __forceinline__ int wave_exclusive_scan(int v, int* total) {
-  const int lane = threadIdx.x;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  *total = __shfl(x, 63, 64);
+  const int x = wave_inclusive(v, 0, [](int a, int b) { return a + b; });
+  *total = lane63(x);
   return x - v;
+}
+
+// Sequences whose slot lies outside the cache or whose length lies outside [0, max_seq_len] (they
+// decode as empty, or may not fit the workspace): counted by the plan from the lengths it reads.
+__device__ int count_bad_seqs(const DecodeParams& p, int t) {
+  int bad = 0;
+  for (int b = t; b < p.batch; b += kPlanThreads) {
+    const int N = p.seq_len[b], slot = p.seq_slot[b];
+    bad += (slot < 0 || slot >= p.num_slots || N < 0 || N > p.max_seq_len) ? 1 : 0;
+  }
+  return wave_sum(bad);
+}
+
+// The header counters: the decode kernels add to the first three.
+__device__ void write_counters(const DecodeParams& p, int t, int bad) {
+  if (t == 0) {
+    p.plan_hdr[kHdrGiveUps] = 0;  // the decode kernels add to these three
+    p.plan_hdr[kHdrBadPages] = 0;
+    p.plan_hdr[kHdrDirect] = 0;
+    p.plan_hdr[kHdrBadSeqs] = bad;
+  }
 }
 
 // The plan for batch <= kPlanThreads * kPlanRegs: every sequence's length is read once into lane
@@ -52,9 +104,10 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
     sv[k] = has[k] ? p.seq_slot[b] : 0;
   }
   long long local = 0;
-  int n_max = 0;
+  int n_max = 0, bad = 0;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
+    bad += has[k] && (sv[k] < 0 || sv[k] >= p.num_slots || Nv[k] < 0 || Nv[k] > p.max_seq_len);
     const int N = (sv[k] < 0 || sv[k] >= p.num_slots) ? 0 : Nv[k];
     const int p_lo = p.n_sink, p_hi = N - p.n_recent;
     fpg[k] = p_lo / kPageTokens;
@@ -63,11 +116,9 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
     local += npk[k] + (nbt[k] + kPageTokens - 1) / kPageTokens;
     n_max = std::max(n_max, npk[k]);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    local += __shfl_xor(local, d, 64);
-    n_max = std::max(n_max, __shfl_xor(n_max, d, 64));
-  }
+  local = wave_sum(local);
+  n_max = wave_max(n_max, 0);
+  write_counters(p, t, wave_sum(bad));
   int pps = (int)std::min<long long>((local + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
   // target_items workgroups run at once.  Full chunks plus tails can exceed it by up to batch, and
@@ -82,9 +133,7 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
         if (kPlanThreads * k >= p.batch) break;  // (integer divisions are not cheap)
         n += (npk[k] + c - 1) / c;
       }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
-      return n;
+      return wave_sum(n);
     };
     int lo = pps, hi = std::min(std::max(n_max, pps), pps + pps / 4);
     if (items_at(lo) > p.target_items && items_at(hi) <= p.target_items) {
@@ -138,6 +187,7 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
         const int other = __builtin_amdgcn_readlane(tp[k2], src), b2 = src + kPlanThreads * k2;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+          if (k >= n_groups) break;
           const int mine = tp[k], b = t + kPlanThreads * k;
           ranks[k] += other > mine || (other == mine && other > 0 && b2 < b);
         }
@@ -173,40 +223,21 @@ __device__ void plan_in_registers(const DecodeParams& p, int t) {
   }
 }
 
-// Sequences whose slot lies outside the cache or whose length lies outside [0, max_seq_len] (they
-// decode as empty, or may not fit the workspace); written to the header with the other counters.
-__device__ void write_counters(const DecodeParams& p, int t) {
-  int bad = 0;
-  for (int b = t; b < p.batch; b += kPlanThreads) {
-    const int N = p.seq_len[b], slot = p.seq_slot[b];
-    bad += (slot < 0 || slot >= p.num_slots || N < 0 || N > p.max_seq_len) ? 1 : 0;
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
-  if (t == 0) {
-    p.plan_hdr[kHdrGiveUps] = 0;  // the decode kernels add to these three
-    p.plan_hdr[kHdrBadPages] = 0;
-    p.plan_hdr[kHdrDirect] = 0;
-    p.plan_hdr[kHdrBadSeqs] = bad;
-  }
-}
-
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   const int t = threadIdx.x;
-  write_counters(p, t);
   if (p.batch <= kPlanThreads * kPlanRegs) {
     plan_in_registers(p, t);
     return;
   }
   // larger batches: the sequences are read per pass, chunks of P = ceil(total pages / target
   // items) pages, tails in sequence order
+  write_counters(p, t, count_bad_seqs(p, t));
   long long local = 0;
   for (int b = t; b < p.batch; b += kPlanThreads) {
     int fp;
     local += seq_packed_pages(p, b, &fp) + seq_bf16_pages(p, b);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) local += __shfl_xor(local, d, 64);
+  local = wave_sum(local);
   int pps = (int)std::min<long long>((local + p.target_items - 1) / std::max(1, p.target_items), 1 << 20);
   pps = std::max(pps, p.min_pages_per_split);
   if (p.force_pages_per_split > 0) pps = p.force_pages_per_split;
@@ -273,21 +304,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
 // w, w + 4, ... over all 512 channels (8 per lane), eight rows at a time with every load
 // requested before use, as a running max-shifted sum; the four waves' sums are then joined
 // through LDS.
-constexpr int kCombineWaves = 4;  // waves per workgroup
-// rw waves per output row (sequence b, head h), 4 / rw rows per workgroup: wave w takes row
-// blockIdx.x * (4 / rw) + w / rw and, of that row's partials (one per work item of the sequence),
+// rw waves per output row (sequence b, head h), W / rw rows per workgroup of W waves: wave w takes
+// row blockIdx.x * (W / rw) + w / rw and, of that row's partials (one per work item of the sequence),
 // those with index = w % rw modulo rw, eight at a time, merged with a running max; the waves of a
 // row are joined through LDS.  Lane l holds channels 4 l .. 4 l + 3 (group l / 16) and
-// 256 + 4 l .. (group 4 + l / 16).  rw (1, 2 or 4) is chosen on the host so that a launch has a
-// few thousand waves in flight: one per row when the rows are many, four when they are few (and
-// their partials many).
-__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(DecodeParams p, int rw) {
+// 256 + 4 l .. (group 4 + l / 16).  rw (1 .. 16, a power of two) is chosen on the host so that a
+// launch has a few thousand waves in flight and a wave merges about one batch of partials: one
+// wave per row when the rows are many, up to sixteen when they are few (and their partials many).
+template <int W>
+__global__ __launch_bounds__(64 * W) void combine_kernel(DecodeParams p, int rw) {
   constexpr int kBatch = 8;
-  __shared__ float sh_m[kCombineWaves], sh_d[kCombineWaves];
-  __shared__ f32x4 sh_acc[kCombineWaves][2][64];
+  __shared__ float sh_m[W], sh_d[W];
+  __shared__ f32x4 sh_acc[W][2][64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = w % rw, w0 = w - sub;  // w0: the row's first wave
-  const int64_t rid = (int64_t)blockIdx.x * (kCombineWaves / rw) + w / rw;
+  const int64_t rid = (int64_t)blockIdx.x * (W / rw) + w / rw;
   const bool live = rid < (int64_t)p.batch * p.heads;
   const int b = live ? (int)(rid / p.heads) : 0;
   const int h = live ? (int)(rid % p.heads) : 0;
@@ -395,13 +426,22 @@ hipError_t launch_plan(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.heads;
   if (rows == 0) return hipSuccess;
-  const int rw = rows >= 4096 ? 1 : rows >= 2048 ? 2 : 4;  // waves per row
-  const int64_t blocks = (rows * rw + kCombineWaves - 1) / kCombineWaves;
+  // waves per row: at least 2,048 waves in all, and (as far as 16 waves go) at most 8 partials per
+  // wave, taking max_items / batch for a row's partial count
+  const int64_t per_row = ((int64_t)p.max_items + p.batch - 1) / p.batch;
+  int rw = 1;
+  while (rw < 16 && (rows * rw < 2048 || 8 * rw < per_row)) rw *= 2;
   DecodeParams arg = p;
   int rw_arg = rw;
   void* args[] = {&arg, &rw_arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(combine_kernel), dim3((unsigned)blocks),
-                         dim3(64 * kCombineWaves), args, 0, stream);
+  if (rw <= 4) {
+    const int64_t blocks = (rows * rw + 3) / 4;
+    return hipLaunchKernel(reinterpret_cast<const void*>(combine_kernel<4>), dim3((unsigned)blocks), dim3(64 * 4),
+                           args, 0, stream);
+  }
+  const int64_t blocks = (rows * rw + 15) / 16;
+  return hipLaunchKernel(reinterpret_cast<const void*>(combine_kernel<16>), dim3((unsigned)blocks), dim3(64 * 16),
+                         args, 0, stream);
 }
 
 }  // namespace mla
