@@ -83,11 +83,15 @@ struct MergeArea {          // merge of the pairs' partials at the end (two pair
 constexpr int kPB = 32;    // tokens per packed block
 constexpr int kVS = 528;   // code tile row stride (bytes): 33 units of 16, odd, so the same unit of
                            // 16 consecutive rows falls in distinct banks
+// Row strides of the small per-block buffers, chosen for the LDS banks: the QK wave's 8-byte
+// probability writes (16 token rows per pass) and 2-byte scale / zero writes cover distinct banks.
+constexpr int kPkP = 20;   // probability row stride (halves)
+constexpr int kPkS = 48;   // PV scale / zero row stride (halves)
 struct __align__(16) PkBuf {
   uint8_t V[kPB][kVS];     // code bytes [token][unit order]
-  f16 P[kPB][16];          // fp16 probabilities [token][head]
-  f16 SV[8][kPB];          // PV scales s_g * 2^-E [group][token]; 0 for masked tokens
-  f16 Z[8][kPB];           // zeros z_g [group][token]; 0 for masked tokens
+  f16 P[kPB][kPkP];        // fp16 probabilities [token][head]
+  f16 SV[8][kPkS];         // PV scales s_g * 2^-E [group][token]; 0 for masked tokens
+  f16 Z[8][kPkS];          // zeros z_g [group][token]; 0 for masked tokens
   float alpha[16];         // per-head factor for the PV accumulators before this block
   int resc;                // bit 0: apply alpha before this block; bit 1: the PV scale exponent changed
   int pv_exp;              // E: the block's PV scales are fp16(s * 2^-E) (valid with bit 1 of resc)
@@ -233,10 +237,12 @@ template <int BITS_C>
 __device__ __forceinline__ constexpr int pk_unit_off(int b) {
   return BITS_C == 4 ? 8 * (b >> 3) + 2 * (b & 3) + ((b >> 2) & 1) : 4 * (b & 3) + (b >> 2);
 }
-// the four units of group g (g < 8): unit qk_unit(g, q) is the one QK lanes 16 q .. 16 q + 15 multiply
+// the four units of group g (g < 8): unit qk_unit(g, q) is the one QK lanes 16 q .. 16 q + 15 multiply.
+// Lane groups q = 0, 1 (and 2, 3) share the passes of a 16-byte LDS read; their units lie 16 apart,
+// i.e. 64 dwords, so that with the 132-dword row stride the 16 rows of both fall on distinct banks.
 template <int BITS_C>
 __device__ __forceinline__ constexpr int qk_unit(int g, int q) {
-  return BITS_C == 4 ? 16 * (q >> 1) + 2 * g + (q & 1) : 16 * (q >> 1) + 8 * (q & 1) + g;
+  return BITS_C == 4 ? 16 * (q & 1) + 2 * g + (q >> 1) : 16 * (q & 1) + 8 * (q >> 1) + g;
 }
 
 // 8 nibbles -> 8 code bytes (channels 0 2 4 6 | 1 3 5 7 of the dword)
@@ -649,8 +655,8 @@ __device__ __forceinline__ void packed_item(const DecodeParams& p, Tiles16& s_ti
       const lds_ptr<uint8_t> vb = lds_opaque(&B.V[0][0]);
       const lds_ptr<f16> pp = lds_opaque(&B.P[0][0]);
       // B operand base: tokens 8 G .. 8 G + 7 of head L16 (two 4-token transposed reads)
-      const f16x8 pv = cat8(lds_tr4(pp + (8 * G + (L16 >> 2)) * 16 + 4 * (L16 & 3)),
-                            lds_tr4(pp + (8 * G + 4 + (L16 >> 2)) * 16 + 4 * (L16 & 3)));
+      const f16x8 pv = cat8(lds_tr4(pp + (8 * G + (L16 >> 2)) * kPkP + 4 * (L16 & 3)),
+                            lds_tr4(pp + (8 * G + 4 + (L16 >> 2)) * kPkP + 4 * (L16 & 3)));
       const int resc = __builtin_amdgcn_readfirstlane(B.resc);
       if (resc) {
         const float a = (resc & 1) ? B.alpha[L16] : 1.f;
