@@ -27,22 +27,47 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Cross-lane reductions with DPP row operations (plain VALU instructions; a ds_bpermute shuffle
+// costs an LDS round trip and each group's quantizer is a chain of such steps).  A lane whose DPP
+// source lies outside its 16-lane row, or in a row outside the row mask, takes the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float x, float identity) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// OR over each aligned group of W (8 or 16) consecutive lanes, complete in the group's first lane:
+// lane i ORs lanes i + 1, i + 2, i + 4 (, i + 8) of its row (row_shl)
 template <int W>
 __device__ __forceinline__ uint32_t or_reduce(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < W; o <<= 1) v |= __shfl_xor(v, o, 64);
+  v |= dpp_u<0x101, 0xf>(v, 0u);
+  v |= dpp_u<0x102, 0xf>(v, 0u);
+  v |= dpp_u<0x104, 0xf>(v, 0u);
+  if (W == 16) v |= dpp_u<0x108, 0xf>(v, 0u);
   return v;
 }
 
+// min / max over the 64 lanes (every lane gets the result): an inclusive scan in lane order (row
+// shifts by 1, 2, 4, 8, then row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3),
+// whose last lane holds the whole
+template <typename Op>
+__device__ __forceinline__ float wave_scan_last(float x, float identity, Op op) {
+  x = op(x, dpp_f<0x111, 0xf>(x, identity));
+  x = op(x, dpp_f<0x112, 0xf>(x, identity));
+  x = op(x, dpp_f<0x114, 0xf>(x, identity));
+  x = op(x, dpp_f<0x118, 0xf>(x, identity));
+  x = op(x, dpp_f<0x142, 0xa>(x, identity));
+  x = op(x, dpp_f<0x143, 0xc>(x, identity));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_scan_last(v, __builtin_inff(), [](float a, float b) { return fminf(a, b); });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_scan_last(v, -__builtin_inff(), [](float a, float b) { return fmaxf(a, b); });
 }
 
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
@@ -80,7 +105,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 
   if (prow_c) {
-#pragma unroll 1
+#pragma unroll
     for (int g = 0; g < kGroups; ++g) {
       const int bits = g < 8 ? p.bits_c : 4;
       const int lb = (1 << bits) - 1;
