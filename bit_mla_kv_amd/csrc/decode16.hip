@@ -118,11 +118,17 @@ __device__ __forceinline__ f32x4 mfma32k(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16k(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+// (max: DPP within the row, lanes i ^ 1 and i ^ 2 (quad_perm), then the mirrored lane of the half
+// row and of the row; every lane ends with the row's maximum, and no LDS round trip is taken)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 64));
-  v = fmaxf(v, __shfl_xor(v, 2, 64));
-  v = fmaxf(v, __shfl_xor(v, 4, 64));
-  return fmaxf(v, __shfl_xor(v, 8, 64));
+  v = fmaxf(v, dpp_row<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_row<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_row<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_row<0x140>(v));  // row_mirror
 }
 __device__ __forceinline__ float row16_sum(float v) {
   v += __shfl_xor(v, 1, 64);

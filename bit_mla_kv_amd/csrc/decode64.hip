@@ -171,18 +171,18 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-// max / sum over the 16 lanes of a row (lanes 16k .. 16k + 15)
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 64));
-  v = fmaxf(v, __shfl_xor(v, 2, 64));
-  v = fmaxf(v, __shfl_xor(v, 4, 64));
-  return fmaxf(v, __shfl_xor(v, 8, 64));
+// max over the 16 lanes of a row (lanes 16k .. 16k + 15)
+// (max: DPP within the row, lanes i ^ 1 and i ^ 2 (quad_perm), then the mirrored lane of the half
+// row and of the row; every lane ends with the row's maximum, and no LDS round trip is taken)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  return v + __shfl_xor(v, 8, 64);
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_row<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_row<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_row<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_row<0x140>(v));  // row_mirror
 }
 
 template <int BITS_C>
