@@ -17,7 +17,7 @@
 //    outside the item) and takes the group-scaled sum as its accumulator, so
 //    the score leaves it complete.  Online softmax in the log2 domain with a
 //    lazily refreshed running max; probabilities are published to LDS as fp16
-//    [token][head].
+//    [token][head], token rows permuted for the LDS banks (p_row below).
 //    The same waves also load the packed bytes of the tile three steps ahead
 //    into registers and unpack the next tile into an fp16 tile of exact codes
 //    (nibbles / crumbs become fp8 bytes whose e4m3 value is code * 2^-9,
@@ -34,7 +34,8 @@
 // step k the QK waves score tile k (MFMAs first, then the softmax and their
 // share of the unpacking of tile k + 1) and the PV waves accumulate tile k - 1
 // (their unpacking first, then the MFMAs), so that each role's VALU work meets
-// the other's MFMAs on the shared SIMD.
+// the other's MFMAs on the shared SIMD.  The token order of each MFMA's k slots
+// is chosen so that the LDS accesses of a step fall on distinct banks.
 // Partials are left unnormalised with their running max and sum; the combine
 // kernel adds the zero terms and merges splits.  A sequence decoded in one item
 // gets its final outputs and lse here instead.
