@@ -151,10 +151,35 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
+def _code_only(text):
+    """C/C++ source without its comments and blank lines (string literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':  # string literal: copied through its closing quote
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def source_digest():
+    """Digest of the decode kernels' code (comments and blank lines excluded): the committed counter
+    summaries name the digest of the code they were taken on."""
     h = hashlib.sha256()
     for f in ("decode.hip", "decode64.hip", "decode16.hip", "decode_common.h", "mla_internal.h"):
-        h.update(open(os.path.join(ROOT, "bit_mla_kv_amd", "csrc", f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "bit_mla_kv_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,3 +38,16 @@ def test_algorithmic_work_of_the_headline_decode():
     # short sequences are read from bf16 only
     by_s, fl_s = b.algorithmic([100], 16, 2)
     assert by_s == 1152 * 100 + 4 * 2 + 16 * 2180 and fl_s == 2 * 16 * 1088 * 100
+
+
+def test_source_digest_ignores_comments_only():
+    """The digest that ties a committed counter summary to the kernel code it was taken on changes
+    with the code, not with its comments or blank lines; string literals are kept whole."""
+    b = _bench_module()
+    code = 'int a = 1;\nasm volatile("s_nop 0" ::: "memory");\nint b = a + 2;\n'
+    commented = ('// header\nint a = 1;  // one\n\n/* block\n   comment */\n'
+                 'asm volatile("s_nop 0" ::: "memory");\nint b = a + 2;  /* two */\n')
+    assert b._code_only(code) == b._code_only(commented)
+    assert b._code_only(code) != b._code_only(code.replace("a + 2", "a + 3"))
+    assert b._code_only('const char* s = "x // y /* z */";') == 'const char* s = "x // y /* z */";'
+    assert len(b.source_digest()) == 16
