@@ -544,3 +544,28 @@ def test_decode_value_range(cache_mult, q_mult, bits_c, heads):
     out, lse = run_decode(cache, q, lens)
     ro, rl = reference(rows, q, bits_c, SCALE)
     check(out, lse, ro, rl, f"cache x{cache_mult} q x{q_mult:.3g} C{bits_c} H{heads}")
+
+
+def _random_config(seed):
+    rng = np.random.default_rng(1000 + seed)
+    heads = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    bits_c = int(rng.choice([4, 2]))
+    B = int(rng.integers(1, 25))
+    lens = [int(x) for x in np.exp(rng.uniform(0, np.log(20000), size=B)).astype(np.int64) - 1]
+    n_sink, n_recent = [(4, 128), (0, 17), (9, 300), (4, 1)][int(rng.integers(0, 4))]
+    return heads, bits_c, lens, n_sink, n_recent
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_configs(seed):
+    """Seeded random shapes against the oracle on every (sequence, head) row: head count (both
+    kernels), bit width, batch 1..24, log-uniform lengths 0..20K (so the plan mixes full chunks,
+    tails and bf16 items, and the combine one or several partials per row) and sink / recent
+    window sizes."""
+    heads, bits_c, lens, n_sink, n_recent = _random_config(seed)
+    rows = [mi.rows(2000 + seed, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(2000 + seed, len(lens), heads)
+    cache = build(rows, bits_c, seed=2000 + seed, n_sink=n_sink, n_recent=n_recent)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = reference(rows, q, bits_c, SCALE, n_sink=n_sink, n_recent=n_recent)
+    check(out, lse, ro, rl, f"seed {seed}: H{heads} C{bits_c} B{len(lens)} sink {n_sink} recent {n_recent}")
