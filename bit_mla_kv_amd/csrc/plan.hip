@@ -306,14 +306,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
 // through LDS.
 // rw waves per output row (sequence b, head h), W / rw rows per workgroup of W waves: wave w takes
 // row blockIdx.x * (W / rw) + w / rw and, of that row's partials (one per work item of the sequence),
-// those with index = w % rw modulo rw, eight at a time, merged with a running max; the waves of a
+// those with index = w % rw modulo rw, four at a time, merged with a running max; the waves of a
 // row are joined through LDS.  Lane l holds channels 4 l .. 4 l + 3 (group l / 16) and
 // 256 + 4 l .. (group 4 + l / 16).  rw (1 .. 16, a power of two) is chosen on the host so that a
 // launch has a few thousand waves in flight and a wave merges about one batch of partials: one
 // wave per row when the rows are many, up to sixteen when they are few (and their partials many).
 template <int W>
 __global__ __launch_bounds__(64 * W) void combine_kernel(DecodeParams p, int rw) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;  // partials requested together: 4 keeps the kernel at 74 VGPRs, 6-7 waves
+                              // per SIMD, which beat 8 (114 VGPRs, 4 waves) on every shape measured
   __shared__ float sh_m[W], sh_d[W];
   __shared__ f32x4 sh_acc[W][2][64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
