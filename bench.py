@@ -197,6 +197,21 @@ def committed_traffic(workload):
     return float(m_val.group(1))
 
 
+def committed_mfma_busy(workload):
+    """Fraction of the matrix cores' cycles busy during the decode kernel (SQ_VALU_MFMA_BUSY_CYCLES
+    over 1024 SIMDs x 2.4 GHz x the kernel's duration), from the committed rocprofv3 SQ counter
+    summary, if it was taken on the current decode source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"decode source digest: `([0-9a-f]+)`", txt)
+    m_row = re.search(r"^\| `decode(?:64|16)_kernel<\d>` \|.*\| ([0-9.]+) \|$", txt, re.M)
+    if not (m_src and m_row) or m_src.group(1) != source_digest():
+        return None
+    return float(m_row.group(1))
+
+
 def bf16_sweep(args):
     """Decode latency of a C4R4 cache vs an all-bf16 cache (n_recent >= N) on the same kernels.
     Every sequence holds the same synthetic rows (the timing does not depend on the values); both
@@ -460,6 +475,7 @@ def main():
         "decode_kernel_ms": round(k_avg_ms, 5), "decode_kernel_ms_p10_p90": [round(float(np.percentile(k_ms, 10)), 5),
                                                                            round(float(np.percentile(k_ms, 90)), 5)],
         "roofline": roof,
+        "mfma_busy_counter": committed_mfma_busy(args.workload),
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1), "wall_s_timed": round(wall, 3),
     }

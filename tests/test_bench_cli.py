@@ -51,3 +51,16 @@ def test_source_digest_ignores_comments_only():
     assert b._code_only(code) != b._code_only(code.replace("a + 2", "a + 3"))
     assert b._code_only('const char* s = "x // y /* z */";') == 'const char* s = "x // y /* z */";'
     assert len(b.source_digest()) == 16
+
+
+def test_committed_counter_summaries_match_the_current_kernels():
+    """The bench line's traffic and MFMA-busy figures come from the committed rocprofv3 summaries; they
+    are taken on the current decode source, so both are present for the headline workload and agree
+    with the table rows they are read from."""
+    b = _bench_module()
+    traffic = b.committed_traffic("dsv3_c4r4_128k")
+    busy = b.committed_mfma_busy("dsv3_c4r4_128k")
+    assert traffic is not None and 3.0e8 < traffic < 6.0e8
+    assert busy is not None and 0.0 < busy < 1.0
+    assert b.committed_mfma_busy("dsv2lite_c4r4_128k") is not None
+    assert b.committed_mfma_busy("no_such_workload") is None
