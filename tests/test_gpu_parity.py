@@ -244,6 +244,20 @@ def test_decode_heads_256():
     check(out, lse, ro, rl, "H256")
 
 
+@pytest.mark.parametrize("heads,bits_c", [(192, 2), (192, 4), (80, 4), (112, 2)])
+def test_decode_odd_head_group_counts(heads, bits_c):
+    """Head counts whose groups do not pair up: three 64-head groups (192, the 64-head kernel) and five
+    or seven 16-head groups (80, 112), so the grid's head-group index and the XCD-interleaved item
+    index take every residue; every (sequence, head) row against the oracle."""
+    lens = [0, 133, 2500, 7000]
+    rows = [mi.rows(43, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(43, len(lens), heads)
+    cache = build(rows, bits_c, seed=43)
+    out, lse = run_decode(cache, q, lens)
+    ro, rl = reference(rows, q, bits_c, SCALE)
+    check(out, lse, ro, rl, f"H{heads} C{bits_c}")
+
+
 def test_all_bf16_mode():
     """n_recent >= N: every token from bf16, equals standard attention (oracle in all-bf16 mode)."""
     lens = [300, 1000]
