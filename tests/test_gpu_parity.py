@@ -258,6 +258,19 @@ def test_decode_odd_head_group_counts(heads, bits_c):
     check(out, lse, ro, rl, f"H{heads} C{bits_c}")
 
 
+@pytest.mark.parametrize("heads", [16, 128])
+def test_decode_max_len_far_above_lengths(heads):
+    """max_seq_len of 2^20 with short sequences: the host sizes the workspace and the grid for the
+    bound, the device plan splits only the tokens present, and the surplus workgroups find no item."""
+    lens = [5, 900, 3000]
+    rows = [mi.rows(44, b, n) for b, n in enumerate(lens)]
+    q = mi.queries(44, len(lens), heads)
+    cache = build(rows, 4, seed=44)
+    out, lse = run_decode(cache, q, lens, max_len=1 << 20)
+    ro, rl = reference(rows, q, 4, SCALE)
+    check(out, lse, ro, rl, f"H{heads} max_len 2^20")
+
+
 def test_all_bf16_mode():
     """n_recent >= N: every token from bf16, equals standard attention (oracle in all-bf16 mode)."""
     lens = [300, 1000]
