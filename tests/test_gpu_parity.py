@@ -271,6 +271,29 @@ def test_decode_max_len_far_above_lengths(heads):
     check(out, lse, ro, rl, f"H{heads} max_len 2^20")
 
 
+@pytest.mark.parametrize("heads", [16, 128])
+def test_decode_permuted_and_repeated_slots(heads):
+    """A batch that reads the cache slots out of order, one slot twice (with different queries) and
+    leaves one slot unread: each batch entry attends over its own slot's tokens."""
+    slot_lens = [300, 0, 2500, 133, 77]
+    rows = [mi.rows(45, s_, n) for s_, n in enumerate(slot_lens)]
+    cache = build(rows, 4, seed=45)
+    order = [2, 0, 3, 0, 4]
+    lens = [slot_lens[s_] for s_ in order]
+    q_u16 = mi.queries(45, len(order), heads)
+    dev = cache.pages.device
+    B, H = len(order), heads
+    q = cb.to_device_bf16(q_u16.reshape(B * H, -1), dev).view(B, H, 576)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = m.alloc_workspace(cache.layout, B, H, max(lens), dev)
+    m.decode(cache, q, torch.tensor(order, dtype=torch.int32, device=dev),
+             torch.tensor(lens, dtype=torch.int32, device=dev), max(lens), SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = reference([rows[s_] for s_ in order], q_u16, 4, SCALE)
+    check(out, lse, ro, rl, f"H{heads} slots {order}")
+
+
 def test_all_bf16_mode():
     """n_recent >= N: every token from bf16, equals standard attention (oracle in all-bf16 mode)."""
     lens = [300, 1000]
